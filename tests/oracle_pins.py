@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle against facts fixed outside it.
+
+Each ``pin_*`` takes the oracle module (``orc``) and raises AssertionError when
+the oracle disagrees with a closed form, a library routine, an invariant or a
+brute-force computation.  ``test_oracle_pins.py`` runs them on the real
+oracle; ``test_oracle_mutations.py`` runs them on copies of the oracle with a
+planted mistake and requires that every mistake is caught.
+
+None of these checks re-types the oracle's formula: masks are checked against
+closed forms, a hand-worked example and boolean matrix-power reachability;
+attention is checked against torch's CPU fp64 ``scaled_dot_product_attention``
+(with an explicit boolean mask), scipy's ``logsumexp``, closed forms for
+uniform keys and a one-node tree, scalar loops, and invariances.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+from workloads import make_tree, make_workload
+
+TOL = 1e-12
+
+
+def _closure(parent_row: np.ndarray) -> np.ndarray:
+    """Reachability by boolean matrix powers: R = (I + P)^T > 0 where
+    P[i, parent(i)] = 1.  R[i, j] iff j is reachable from i by parent steps."""
+    T = len(parent_row)
+    A = np.eye(T, dtype=np.int64)
+    for i, p in enumerate(parent_row):
+        if p >= 0:
+            A[i, p] = 1
+    R = np.eye(T, dtype=np.int64)
+    for _ in range(max(T, 1)):
+        R = np.minimum(R @ A, 1)
+    return R.astype(bool)
+
+
+def _unpack(mask_words: np.ndarray, T: int) -> np.ndarray:
+    """uint64 [T, W] -> bool [T, T] (bit j%64 of word j//64)."""
+    out = np.zeros((T, T), dtype=bool)
+    for i in range(T):
+        for j in range(T):
+            out[i, j] = (int(mask_words[i, j // 64]) >> (j % 64)) & 1
+    return out
+
+
+# ----------------------------------------------------------------- masks
+
+def pin_mask_hand_example(orc):
+    """A small forest worked by hand from the ancestor-or-self definition."""
+    parent = np.array([[-1, 0, 0, 1, 1, 2, -1, 6]], dtype=np.int32)
+    expect = [{0}, {0, 1}, {0, 2}, {0, 1, 3}, {0, 1, 4}, {0, 2, 5}, {6}, {6, 7}]
+    m = orc.oracle_mask(parent)
+    assert m.shape == (1, 8, 1) and m.dtype == np.uint64
+    for i, s in enumerate(expect):
+        assert int(m[0, i, 0]) == sum(1 << j for j in s), (i, bin(int(m[0, i, 0])))
+
+
+def pin_mask_chain_and_star(orc):
+    """Chain: row i = bits 0..i (lower-triangular).  Star: row i = {0, i}.
+    T = 70 crosses a 64-bit word boundary."""
+    for T in (1, 2, 8, 63, 64, 65, 70):
+        chain = np.array([[-1] + list(range(T - 1))], dtype=np.int32)
+        m = orc.oracle_mask(chain)
+        assert m.shape == (1, T, (T + 63) // 64)
+        assert np.array_equal(_unpack(m[0], T), np.tril(np.ones((T, T), bool)))
+        star = np.array([[-1] + [0] * (T - 1)], dtype=np.int32)
+        m = orc.oracle_mask(star)
+        want = np.eye(T, dtype=bool)
+        want[:, 0] = True
+        assert np.array_equal(_unpack(m[0], T), want)
+
+
+def pin_mask_exhaustive_small(orc):
+    """Every parent array with parent[i] in [-1, i-1] for T <= 6 (873 trees and
+    forests) against matrix-power reachability, plus popcount == depth where
+    depth is counted by the recursion depth(i) = 1 + depth(parent(i))."""
+    for T in range(1, 7):
+        for choice in itertools.product(*[range(-1, i) for i in range(T)]):
+            p = np.array([choice], dtype=np.int32)
+            got = _unpack(orc.oracle_mask(p)[0], T)
+            assert np.array_equal(got, _closure(p[0])), choice
+            depth = []
+            for i in range(T):
+                depth.append(1 if p[0, i] < 0 else depth[p[0, i]] + 1)
+            assert list(got.sum(axis=1)) == depth, choice
+
+
+def pin_mask_random_recursion(orc):
+    """Random trees up to T = 64: row(i) == row(parent(i)) | bit(i) on the
+    packed words, and a root row is just its own bit."""
+    rng = np.random.default_rng(7)
+    for T in (16, 33, 64):
+        for kind in ("uniform", ("bounded", 6, 4), "forest"):
+            p = make_tree(rng, T, kind)[None, :]
+            m = orc.oracle_mask(p)[0, :, 0]
+            for i in range(T):
+                parent_row = int(m[p[0, i]]) if p[0, i] >= 0 else 0
+                assert int(m[i]) == parent_row | (1 << i)
+
+
+def pin_check_parent(orc):
+    """Entries outside [-1, i-1] are reported by flat index, in order."""
+    p = np.array([[-1, 0, 2, 1], [0, -1, -2, 3]], dtype=np.int32)
+    assert orc.check_parent(p) == [2, 4, 6, 7]
+    assert orc.check_parent(np.array([[-1, 0, 1, 0]], dtype=np.int32)) == []
+
+
+# ----------------------------------------------------------- attention
+
+def _case(seed, B=2, T=6, Hq=4, Hkv=2, D=8, prefix_lens=(5, 3), trees="uniform",
+          dtype="f32"):
+    rng = np.random.default_rng(seed)
+    return make_workload(rng, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D,
+                         prefix_lens=list(prefix_lens), trees=trees, dtype=dtype)
+
+
+def _run(orc, w, **over):
+    args = dict(q=w.q, k_prefix=w.k_prefix, v_prefix=w.v_prefix,
+                offsets=w.offsets.numpy(), k_tree=w.k_tree, v_tree=w.v_tree,
+                parent=w.parent.numpy(), scale=w.scale)
+    args.update(over)
+    return orc.oracle_attn(**args)
+
+
+def _sdpa_reference(w, visible_fn):
+    """torch CPU fp64 SDPA over [prefix | tree] per sequence with the boolean
+    mask visible_fn(b, L) -> bool [T, L + T]; GQA by repeating KV heads in
+    contiguous groups.  LSE from scipy.special.logsumexp over the same mask."""
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    G = Hq // Hkv
+    off = w.offsets.numpy()
+    o = np.empty((B, T, Hq, D))
+    lse = np.empty((B, Hq, T))
+    for b in range(B):
+        L = int(off[b + 1] - off[b])
+        k = torch.cat([w.k_prefix[off[b]:off[b + 1]], w.k_tree[b]]).double()
+        v = torch.cat([w.v_prefix[off[b]:off[b + 1]], w.v_tree[b]]).double()
+        k = k.repeat_interleave(G, dim=1).transpose(0, 1).contiguous()  # [Hq, L+T, D]
+        v = v.repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+        q = w.q[b].double().transpose(0, 1).contiguous()                 # [Hq, T, D]
+        vis = torch.from_numpy(visible_fn(b, L))
+        out = torch.nn.functional.scaled_dot_product_attention(
+            q, k, v, attn_mask=vis, scale=w.scale)
+        o[b] = out.transpose(0, 1).numpy()
+        s = (q @ k.transpose(1, 2)).numpy() * w.scale
+        lse[b] = logsumexp(s, axis=-1, b=np.broadcast_to(vis.numpy(), s.shape))
+    return o, lse
+
+
+def _tree_visible(w):
+    parent = w.parent.numpy()
+    T = parent.shape[1]
+
+    def fn(b, L):
+        vis = np.ones((T, L + T), dtype=bool)
+        vis[:, L:] = _closure(parent[b])
+        return vis
+    return fn
+
+
+def pin_general_tree_vs_sdpa(orc):
+    """Random trees (uniform, bounded, forest), ragged prefixes including an
+    empty one, GQA: oracle == torch SDPA with an explicit reachability mask."""
+    for seed, trees, lens, Hq, Hkv in (
+            (1, "uniform", (5, 3), 4, 2),
+            (2, ("bounded", 3, 2), (0, 9), 6, 3),
+            (3, "forest", (4, 1), 4, 4),
+            (4, ["chain", "star"], (7, 2), 8, 2)):
+        w = _case(seed, trees=trees, prefix_lens=lens, Hq=Hq, Hkv=Hkv)
+        o, lse = _run(orc, w)
+        ro, rl = _sdpa_reference(w, _tree_visible(w))
+        assert np.max(np.abs(o - ro)) < TOL, seed
+        assert np.max(np.abs(lse - rl)) < TOL, seed
+
+
+def pin_chain_is_causal(orc):
+    """A chain tree is causal attention over [prefix | tree] with the mask
+    aligned to the bottom right: key j is visible to row i iff j <= L + i."""
+    w = _case(11, T=7, trees="chain", prefix_lens=(6, 0))
+    o, lse = _run(orc, w)
+    T = 7
+
+    def causal(b, L):
+        i = np.arange(T)[:, None]
+        j = np.arange(L + T)[None, :]
+        return j <= L + i
+    ro, rl = _sdpa_reference(w, causal)
+    assert np.max(np.abs(o - ro)) < TOL and np.max(np.abs(lse - rl)) < TOL
+
+
+def pin_single_node_is_decode(orc):
+    """T = 1: one-token decode, softmax(q K^T * scale) V over L + 1 keys,
+    computed here by a plain unmasked SDPA call."""
+    w = _case(12, B=1, T=1, Hq=4, Hkv=2, prefix_lens=(13,))
+    o, lse = _run(orc, w)
+    k = torch.cat([w.k_prefix, w.k_tree[0]]).double()
+    v = torch.cat([w.v_prefix, w.v_tree[0]]).double()
+    for h in range(4):
+        g = h // 2
+        out = torch.nn.functional.scaled_dot_product_attention(
+            w.q[0, :, h][None].double(), k[:, g][None], v[:, g][None], scale=w.scale)
+        assert np.max(np.abs(o[0, 0, h] - out[0, 0].numpy())) < TOL
+        s = (w.q[0, 0, h].double() @ k[:, g].T).numpy() * w.scale
+        assert abs(lse[0, h, 0] - logsumexp(s)) < TOL
+
+
+def pin_uniform_keys(orc):
+    """All keys equal: every visible score is s0 = scale <q, k>, so o is the
+    mean of the visible values and lse = s0 + ln(L + depth(i))."""
+    w = _case(13, B=2, T=6, prefix_lens=(4, 0), trees=("bounded", 3, 2))
+    key = torch.randn(w.k_tree.shape[-1], generator=torch.Generator().manual_seed(0))
+    kp = key.expand_as(w.k_prefix).clone()
+    kt = key.expand_as(w.k_tree).clone()
+    o, lse = _run(orc, w, k_prefix=kp, k_tree=kt)
+    parent = w.parent.numpy()
+    off = w.offsets.numpy()
+    G = w.q.shape[2] // w.k_tree.shape[2]
+    for b in range(2):
+        L = int(off[b + 1] - off[b])
+        reach = _closure(parent[b])
+        for i in range(6):
+            for h in range(w.q.shape[2]):
+                g = h // G
+                vis = [w.v_prefix[off[b] + j, g].double() for j in range(L)]
+                vis += [w.v_tree[b, j, g].double() for j in range(6) if reach[i, j]]
+                mean = torch.stack(vis).mean(0).numpy()
+                s0 = w.scale * float(w.q[b, i, h].double() @ key.double())
+                assert np.max(np.abs(o[b, i, h] - mean)) < TOL
+                assert abs(lse[b, h, i] - (s0 + math.log(len(vis)))) < TOL
+
+
+def pin_brute_force(orc):
+    """Scalar Python loops with math.exp and math.fsum on a tiny case; the
+    visible set is enumerated by following parent links one step at a time."""
+    w = _case(14, B=2, T=5, Hq=4, Hkv=2, D=3, prefix_lens=(3, 0), trees="forest")
+    o, lse = _run(orc, w)
+    q, kp, vp = w.q.double().tolist(), w.k_prefix.double().tolist(), w.v_prefix.double().tolist()
+    kt, vt = w.k_tree.double().tolist(), w.v_tree.double().tolist()
+    parent = w.parent.tolist()
+    off = w.offsets.tolist()
+    for b in range(2):
+        for i in range(5):
+            path, j = [], i
+            while j != -1:
+                path.append(j)
+                j = parent[b][j]
+            for h in range(4):
+                g = h // 2
+                keys = [kp[r][g] for r in range(off[b], off[b + 1])] + [kt[b][j][g] for j in path]
+                vals = [vp[r][g] for r in range(off[b], off[b + 1])] + [vt[b][j][g] for j in path]
+                sc = [w.scale * math.fsum(a * c for a, c in zip(q[b][i][h], kk)) for kk in keys]
+                ex = [math.exp(x) for x in sc]
+                z = math.fsum(ex)
+                assert abs(lse[b][h][i] - math.log(z)) < TOL
+                for d in range(3):
+                    ref = math.fsum(e * vv[d] for e, vv in zip(ex, vals)) / z
+                    assert abs(o[b, i, h, d] - ref) < TOL
+
+
+def pin_split_merge_identity(orc):
+    """Prefix partial (no mask) and tree partial (tree mask) joined by the
+    log-sum-exp merge equal the single pass; each partial equals an SDPA call
+    over its own key set; an empty prefix contributes nothing."""
+    w = _case(15, B=2, T=6, Hq=6, Hkv=2, prefix_lens=(9, 0), trees=("bounded", 4, 2))
+    (op, lp), (ot, lt), (om, lm) = orc.oracle_attn_split(
+        w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(), w.k_tree, w.v_tree,
+        w.parent.numpy(), w.scale)
+    o, lse = _run(orc, w)
+    assert np.max(np.abs(om - o)) < TOL and np.max(np.abs(lm - lse)) < TOL
+    assert np.all(np.isneginf(lp[1]))
+    T = 6
+    ro, rl = _sdpa_reference(w, lambda b, L: np.concatenate(
+        [np.ones((T, L), bool), np.zeros((T, T), bool)], axis=1))
+    assert np.max(np.abs(op[0] - ro[0])) < TOL and np.max(np.abs(lp[0] - rl[0])) < TOL
+    parent = w.parent.numpy()
+    rt, rlt = _sdpa_reference(w, lambda b, L: np.concatenate(
+        [np.zeros((T, L), bool), _closure(parent[b])], axis=1))
+    assert np.max(np.abs(ot - rt)) < TOL and np.max(np.abs(lt - rlt)) < TOL
+
+
+def pin_lse_merge_closed_form(orc):
+    """Two partials with known sums: lse = ln(e^a + e^b) and o is the weighted
+    mean; an empty partial (-inf) is ignored."""
+    a, b = np.array([0.3, -2.0]), np.array([1.1, -2.0])
+    oa, ob = np.array([[1.0, 2.0], [3.0, 4.0]]), np.array([[5.0, 6.0], [7.0, 8.0]])
+    o, lse = orc.lse_merge([(oa, a), (ob, b)])
+    want = np.log(np.exp(a) + np.exp(b))
+    assert np.max(np.abs(lse - want)) < TOL
+    wa = np.exp(a) / (np.exp(a) + np.exp(b))
+    assert np.max(np.abs(o - (wa[:, None] * oa + (1 - wa)[:, None] * ob))) < TOL
+    o2, l2 = orc.lse_merge([(oa, a), (np.full_like(ob, np.nan), np.full(2, -np.inf))])
+    assert np.max(np.abs(o2 - oa)) < TOL and np.max(np.abs(l2 - a)) < TOL
+
+
+def pin_non_ancestor_invariance(orc):
+    """Changing K/V of a tree node outside anc*(i) leaves row i bit-identical."""
+    w = _case(16, B=1, T=8, prefix_lens=(5,), trees="uniform")
+    o, lse = _run(orc, w)
+    reach = _closure(w.parent.numpy()[0])
+    for j in range(8):
+        kt, vt = w.k_tree.clone(), w.v_tree.clone()
+        kt[0, j] += 3.0
+        vt[0, j] -= 2.0
+        o2, l2 = _run(orc, w, k_tree=kt, v_tree=vt)
+        for i in range(8):
+            same = np.array_equal(o2[0, i], o[0, i]) and np.array_equal(l2[0, :, i], lse[0, :, i])
+            assert same == (not reach[i, j]), (i, j)
+
+
+def pin_prefix_permutation(orc):
+    """Permuting prefix rows (K and V together) is invisible up to rounding."""
+    w = _case(17, B=1, T=5, prefix_lens=(11,))
+    o, lse = _run(orc, w)
+    perm = torch.from_numpy(np.random.default_rng(0).permutation(11))
+    o2, l2 = _run(orc, w, k_prefix=w.k_prefix[perm], v_prefix=w.v_prefix[perm])
+    assert np.max(np.abs(o2 - o)) < TOL and np.max(np.abs(l2 - lse)) < TOL
+
+
+def pin_gqa_equals_mha(orc):
+    """GQA with Hkv heads equals MHA with every KV head repeated G times in
+    contiguous order (query head h reads KV head h // G)."""
+    w = _case(18, B=2, T=4, Hq=6, Hkv=2, prefix_lens=(3, 2))
+    o, lse = _run(orc, w)
+    rep = lambda t: t.repeat_interleave(3, dim=-2)  # noqa: E731
+    o2, l2 = _run(orc, w, k_prefix=rep(w.k_prefix), v_prefix=rep(w.v_prefix),
+                  k_tree=rep(w.k_tree), v_tree=rep(w.v_tree))
+    assert np.max(np.abs(o2 - o)) < TOL and np.max(np.abs(l2 - lse)) < TOL
+
+
+def pin_ragged_equals_separate(orc):
+    """A ragged batch equals each sequence run alone."""
+    w = _case(19, B=3, T=4, prefix_lens=(2, 0, 5))
+    o, lse = _run(orc, w)
+    off = w.offsets.numpy()
+    for b in range(3):
+        ob, lb = orc.oracle_attn(
+            w.q[b:b + 1], w.k_prefix[off[b]:off[b + 1]], w.v_prefix[off[b]:off[b + 1]],
+            np.array([0, off[b + 1] - off[b]]), w.k_tree[b:b + 1], w.v_tree[b:b + 1],
+            w.parent.numpy()[b:b + 1], w.scale)
+        assert np.max(np.abs(ob[0] - o[b])) < TOL and np.max(np.abs(lb[0] - lse[b])) < TOL
+
+
+def pin_rows_vs_sdpa(orc):
+    """The per-row form agrees with the SDPA reference on sampled rows."""
+    w = _case(20, B=2, T=6, Hq=4, Hkv=2, prefix_lens=(7, 1), trees=("bounded", 3, 3))
+    ro, rl = _sdpa_reference(w, _tree_visible(w))
+    rows = [(0, 0, 0), (0, 3, 5), (1, 1, 2), (1, 2, 4)]
+    o, lse = orc.oracle_attn_rows(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(),
+                                  w.k_tree, w.v_tree, w.parent.numpy(), w.scale, rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.max(np.abs(o[n] - ro[b, i, h])) < TOL
+        assert abs(lse[n] - rl[b, h, i]) < TOL
+
+
+def pin_bf16_inputs_exact(orc):
+    """bf16 inputs are consumed exactly: the result equals the fp32 run on the
+    same (bf16-representable) values."""
+    w = _case(21, dtype="bf16")
+    o, lse = _run(orc, w)
+    o2, l2 = _run(orc, w, q=w.q.float(), k_prefix=w.k_prefix.float(),
+                  v_prefix=w.v_prefix.float(), k_tree=w.k_tree.float(),
+                  v_tree=w.v_tree.float())
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

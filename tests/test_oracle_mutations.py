@@ -1,0 +1,56 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+that at least one pin catches each.  This shows the pins are strong enough to
+trust the oracle: a dropped term, a wrong sign or index, a transposed operand
+or a wrong head mapping all fail."""
+
+import inspect
+import types
+
+import pytest
+
+import oracle.tree_attention_oracle as orc_src
+from oracle_pins import ALL_PINS
+
+MUTATIONS = {
+    "mask_excludes_self": ("            j = i\n            while j != -1:",
+                           "            j = int(p[b, i])\n            while j != -1:"),
+    "mask_transposed": ("visible[:, L:] = anc[b]", "visible[:, L:] = anc[b].T"),
+    "mask_bit_word": ("out[b, i, j // 64] |=", "out[b, i, 0] |="),
+    "mask_bit_shift": ("np.uint64(j % 64)", "np.uint64(j % 63)"),
+    "scale_dropped": ("s = scale * (q[b, :, h, :] @ keys.T)", "s = (q[b, :, h, :] @ keys.T)"),
+    "lse_drops_max": ("lse = (m + np.log(z))[:, 0]", "lse = np.log(z)[:, 0]"),
+    "o_not_normalised": ("o = (e @ vals) / z", "o = (e @ vals)"),
+    "gqa_interleaved": ("for h in range(g * G, (g + 1) * G):\n                s = scale * (q[b, :, h, :] @ keys.T)\n                o[b, :, h, :]",
+                        "for h in range(g, Hq, Hkv):\n                s = scale * (q[b, :, h, :] @ keys.T)\n                o[b, :, h, :]"),
+    "keys_tree_first": ("keys = np.concatenate([kp[off[b]:off[b + 1], g, :], kt[b, :, g, :]])",
+                        "keys = np.concatenate([kt[b, :, g, :], kp[off[b]:off[b + 1], g, :]])"),
+    "values_from_keys": ("vals = np.concatenate([vp[off[b]:off[b + 1], g, :], vt[b, :, g, :]])",
+                         "vals = np.concatenate([kp[off[b]:off[b + 1], g, :], vt[b, :, g, :]])"),
+    "prefix_from_start": ("keys = np.concatenate([kp[off[b]:off[b + 1], g, :]",
+                          "keys = np.concatenate([kp[0:off[b + 1] - off[b], g, :]"),
+    "parent_allows_self": ("if not (-1 <= int(p[b, i]) <= i - 1):", "if not (-1 <= int(p[b, i]) <= i):"),
+    "merge_unnormalised": ("o = sum((w[k] / z)[..., None]", "o = sum((w[k])[..., None]"),
+    "merge_lse_no_max": ("lse = m + np.log(z)\n", "lse = np.log(z)\n"),
+    "rows_wrong_head": ("        g = h // G\n        kpg", "        g = h % Hkv\n        kpg"),
+}
+
+
+def _mutant(name):
+    src = inspect.getsource(orc_src)
+    old, new = MUTATIONS[name]
+    assert src.count(old) == 1, f"mutation {name} does not apply uniquely"
+    mod = types.ModuleType(f"oracle_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    mod = _mutant(name)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(mod)
+        except Exception:  # AssertionError, or a crash caused by the mistake
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the planted mistake {name}"
