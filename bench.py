@@ -1,0 +1,254 @@
+"""Benchmark of hybrid tree-verification attention on one MI355X.
+
+One step = one ltree_attn call (prefix splits + tree part, then the
+log-sum-exp merge) over the QwQ-32B-shaped layer: batch 1, 40 query heads /
+8 KV heads, head_dim 128, prefix 32768, a 64-node draft tree (depth <= 8,
+branching <= 3), bf16 inputs with 1% of prefix rows scaled x8.  Inputs are
+seeded synthetic data resident in HBM.  Each step reads a different one of
+several copies of the prefix KV cache, together larger than the 256 MB
+Infinity Cache, so every step streams its keys from HBM (cold-cache timing).
+
+Prints one JSON line.  The throughput `value` is algorithmic TFLOP/s of the
+whole call; `roofline` rates the dominant kernel (the partial-attention
+kernel) against the bf16 MFMA peak, with its duration taken from HIP events
+recorded on the launch stream around each of its launches in the timed loop.
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
+on the host cores.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 4]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "tree-verify attn µs/call + TFLOP/s @L=32k,T=64; % MFMA / HBM roofline"
+KERNEL_SOURCES = ["attn_partial_mfma.hip", "ltree_api.hip", "ltree_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partials_qwq32b_L32k_T64.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "tree_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def depth_sum(parent_row) -> int:
+    """Number of (node, visible tree node) pairs = sum of depths."""
+    depth = []
+    for i, p in enumerate(parent_row):
+        depth.append(1 if p < 0 else depth[p] + 1)
+    return sum(depth)
+
+
+def algorithmic_counts(w):
+    """FLOP and HBM bytes the method must move/compute (no split-K partials)."""
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    e = w.q.element_size()
+    sum_l = sum(w.prefix_lens)
+    anc = sum(depth_sum(w.parent[b].tolist()) for b in range(B))
+    flop_prefix = 4 * D * Hq * T * sum_l
+    flop_tree = 4 * D * Hq * anc
+    bytes_ = (2 * sum_l * Hkv * D * e + B * T * Hq * D * e + 2 * B * T * Hkv * D * e
+              + B * T * 8 + B * T * Hq * D * 4 + B * Hq * T * 4 + 4 * (B + 1))
+    # the partial kernel reads q, prefix K/V, tree K/V and the mask
+    bytes_partials = (2 * sum_l * Hkv * D * e + B * T * Hq * D * e + 2 * B * T * Hkv * D * e
+                      + B * T * 8)
+    return flop_prefix + flop_tree, bytes_, bytes_partials
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """fp64 oracle on the first KV heads of the same workload, as many heads as
+    fit in about `budget_s` seconds (at least one)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    G = Hq // Hkv
+    parent = w.parent.numpy()
+    off = w.offsets.numpy()
+    done, flop, t_total = 0, 0, 0.0
+    while done < Hkv and t_total < budget_s:
+        g = done
+        sl = slice(g, g + 1)
+        t0 = time.perf_counter()
+        oracle.oracle_attn(w.q[:, :, g * G:(g + 1) * G], w.k_prefix[:, sl], w.v_prefix[:, sl],
+                           off, w.k_tree[:, :, sl], w.v_tree[:, :, sl], parent, w.scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+        flop += 4 * D * G * T * sum(w.prefix_lens) + 4 * D * G * sum(
+            depth_sum(parent[b].tolist()) for b in range(B))
+        log(f"cpu oracle: {done}/{Hkv} KV heads, {t_total:.1f} s")
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": round(flop / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 NumPy oracle over {done} of {Hkv} KV heads ({done * G} of {Hq} query "
+                  f"heads, all {T} tree rows, full {sum(w.prefix_lens)}-key prefix), "
+                  f"{t_total:.2f} s wall; matmuls on {threads} BLAS threads, exp single-threaded",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--hot", action="store_true", help="reuse one KV copy (cache-resident)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernel shards by KV head or batch with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import CONFIGS, make_config
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    spec = CONFIGS[args.config]
+    log(f"generating workload {spec['name']}")
+    w = make_config(args.config)
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    max_l = max(w.prefix_lens)
+    flop, bytes_alg, bytes_partials = algorithmic_counts(w)
+
+    q = w.q.to(dev)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    offsets = w.offsets.to(dev)
+    parent = w.parent.to(dev)
+    kv_bytes = 2 * w.k_prefix.numel() * w.k_prefix.element_size()
+    n_copies = 1 if args.hot else max(2, math.ceil(512e6 / max(kv_bytes, 1)))
+    kp0, vp0 = w.k_prefix.to(dev), w.v_prefix.to(dev)
+    kv = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(n_copies - 1)]
+    log(f"{n_copies} prefix KV copies of {kv_bytes / 1e6:.1f} MB each")
+
+    # mask: built once per verification step, timed on its own
+    mask = torch.empty((B, T), dtype=torch.int64, device=dev)
+    status = torch.empty((1,), dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        assert ta.ltree_build_mask(parent, mask, status) == 0
+    e0.record()
+    for _ in range(20):
+        ta.ltree_build_mask(parent, mask, status)
+    e1.record()
+    torch.cuda.synchronize()
+    mask_us = e0.elapsed_time(e1) * 1000 / 20
+    assert int(status.item()) == 0
+
+    ws = ta.workspace_for(q, kt, max_l)
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+
+    def step(s, ev_a=None, ev_b=None):
+        kp, vp = kv[s % n_copies]
+        if ev_a is not None:
+            ev_a.record()
+        st = ta.ltree_attn_partials(q, kp, vp, offsets, max_l, kt, vt, mask, ws, w.scale)
+        if ev_b is not None:
+            ev_b.record()
+        st |= ta.ltree_attn_merge(B, T, Hq, Hkv, D, offsets, max_l, o, lse, ws)
+        return st
+
+    log(f"warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        assert step(s) == 0
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s, ev_a[s], ev_b[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000 / K
+    part_us = sum(ev_a[s].elapsed_time(ev_b[s]) for s in range(K)) * 1000 / K
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+    us = ms_per_step * 1000
+    tflops = flop / (us * 1e-6) / 1e12
+    part_tflops = flop / (part_us * 1e-6) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("kernel_hash") == kernel_hash() and rec.get("config") == args.config:
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1); stands in for the pages' long-context datasets)",
+        "config": {
+            "workload": spec["name"], "B": B, "T": T, "Hq": Hq, "Hkv": Hkv, "D": D,
+            "prefix_lens": w.prefix_lens,
+            "cache": "hot (one KV copy)" if args.hot else f"cold ({n_copies} rotating KV copies)",
+        },
+        "us_per_call": round(us, 2),
+        "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "hbm_frac": round(bytes_alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "mask_build_us": round(mask_us, 2),
+        "algorithmic": {"flop": flop, "bytes": bytes_alg},
+        "roofline": {
+            "kernel": "partial_mfma_kernel (prefix splits + tree part)",
+            "bound": "mfma",
+            "achieved": round(part_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(part_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel_us": round(part_us, 2),
+            "hbm_frac": round(bytes_partials / (part_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

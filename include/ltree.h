@@ -1,0 +1,178 @@
+/*
+ * ltree.h -- hybrid tree-verification attention on AMD Instinct MI355X (gfx950).
+ *
+ * A speculative-decoding verifier scores a tree of T draft tokens against a long
+ * cached prefix.  Following the split described on the gist.science page
+ * "LongSpec: Long-Context Lossless Speculative Decoding with Efficient Drafting
+ * and Verification" (section 2 "Methodik", part C "Schnelle Tree Attention"),
+ * the attention of every tree token is computed in two parts:
+ *
+ *   - the cached part: the long prefix KV cache, attended with no mask;
+ *   - the speculative part: the T draft tokens, attended under a tree mask;
+ *
+ * and the two partial softmax results are joined exactly by a log-sum-exp
+ * merge (same section, "Aggregation").  The arXiv abstract of the paper
+ * (mlsanity.com page, section "Abstract (arXiv)") describes the same thing as
+ * fast prefix computation combined with standard tree attention.
+ *
+ * The result equals one softmax over [prefix | tree] in which tree node i sees
+ * every prefix key and the tree nodes in anc*(i) = {i} U ancestors(i):
+ *
+ *     lse[b,h,i] = ln sum_{j visible} exp(scale * <q[b,i,h], k_j>)
+ *     o[b,i,h]   = sum_{j visible} exp(scale * <q[b,i,h], k_j> - lse[b,h,i]) v_j
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  The caller owns all
+ *     buffers; the library never allocates or frees device memory.
+ *   - Every tensor is dense row-major with the last dimension contiguous.
+ *   - Calls are asynchronous on `stream` (0 = the null stream).  The return
+ *     value only reports checks of host-visible arguments and launch errors;
+ *     device-side findings go to the documented device outputs.
+ *   - Query head h reads KV head h / G, with G = Hq / Hkv (contiguous groups).
+ *   - Thread safety: calls may be issued from several host threads; calls that
+ *     share a workspace must be ordered by the caller (same stream, or events).
+ */
+#ifndef LTREE_H
+#define LTREE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LTREE_VERSION 100 /* 1.0.0 */
+#define LTREE_MAX_TREE 64 /* T limit of this version: one 64-bit mask word per row */
+
+typedef enum {
+  LTREE_OK = 0,
+  LTREE_ERR_INVALID_ARG = -1, /* null pointer, bad size, Hq % Hkv != 0, scale <= 0, ... */
+  LTREE_ERR_UNSUPPORTED = -2, /* valid but not built: D not 64/128, T > 64, ...        */
+  LTREE_ERR_WORKSPACE = -3,   /* workspace too small or misaligned                     */
+  LTREE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed            */
+} ltree_status;
+
+typedef enum {
+  LTREE_F32 = 0, /* fp32 q/k/v: exact-arithmetic path (fp32 FMA), for checking */
+  LTREE_BF16 = 1 /* bf16 q/k/v: the MFMA path                                   */
+} ltree_dtype;
+
+/* Library version, LTREE_VERSION of the build. */
+int ltree_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* ltree_status_string(int status);
+
+/*
+ * ltree_build_mask -- ancestor-or-self bitmask of B speculation trees.
+ *
+ * Defines the tree mask of the speculative part (gist.science page, section 2
+ * part C, item 2 of the split; section 1 "Problemstellung", item "Ineffiziente
+ * Verifikation", on tree-attention masks).  A draft token sees its own branch:
+ * itself and its ancestors, no siblings or cousins.
+ *
+ *   parent  [B, T] int32.  parent[b*T+i] = -1 hangs node i directly under the
+ *           prefix; otherwise it is an earlier node, 0 <= parent < i.  Several
+ *           -1 entries (a forest) are allowed.
+ *   B, T    1 <= B, 1 <= T <= LTREE_MAX_TREE.
+ *   mask    [B, T] uint64 out.  Bit j of mask[b*T+i] is set iff j == i or j is
+ *           an ancestor of i.  Bits j >= T are zero.
+ *   status  [1] int32 out, or NULL.  0 when every parent entry is valid; else
+ *           1 + the smallest flat index b*T+i whose entry is invalid.  All mask
+ *           rows of a tree with an invalid entry are written as zero.
+ *
+ * Returns LTREE_OK, LTREE_ERR_INVALID_ARG (null pointer, B < 1, T < 1),
+ * LTREE_ERR_UNSUPPORTED (T > 64) or LTREE_ERR_HIP.  One launch, no workspace.
+ */
+int ltree_build_mask(const int32_t* parent, int B, int T, uint64_t* mask,
+                     int32_t* status, hipStream_t stream);
+
+/*
+ * ltree_attn_workspace_bytes -- size of the scratch buffer `ltree_attn`,
+ * `ltree_attn_partials` and `ltree_attn_merge` need for these sizes on the
+ * current device.  The workspace holds the fp32 partial results of the prefix
+ * splits and of the tree part.  Returns 0 if the sizes are invalid.
+ */
+size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
+                                  int max_prefix_len);
+
+/*
+ * ltree_attn -- hybrid tree-verification attention, all three steps.
+ *
+ * Step 1 (cached part, gist.science section 2 part C item 1): every tree
+ * query attends the whole prefix of its sequence with no mask.  The prefix is
+ * cut into splits that run in parallel; each split yields a normalised partial
+ * output and its log-sum-exp.  Step 2 (speculative part, item 2): every tree
+ * query attends the T tree tokens under `mask`.  Step 3 ("Aggregation"): all
+ * partials are joined by a log-sum-exp merge into `o` and `lse`.
+ *
+ *   dtype          LTREE_BF16 or LTREE_F32 for q, k_prefix, v_prefix, k_tree, v_tree.
+ *   B, T, Hq, Hkv, D
+ *                  batch, tree size (1..64), query heads, KV heads (Hq % Hkv == 0),
+ *                  head dim (64 or 128).
+ *   scale          score scale (usually 1/sqrt(D)); finite and > 0.
+ *   q              [B, T, Hq, D] queries of the tree tokens (after RoPE).
+ *   k_prefix, v_prefix
+ *                  [sum_b L_b, Hkv, D] packed prefix cache; sequence b owns rows
+ *                  prefix_offsets[b] .. prefix_offsets[b+1]-1.
+ *   prefix_offsets [B+1] int32, offsets[0] = 0, non-decreasing; L_b may be 0.
+ *   max_prefix_len host int >= every L_b; it sizes the grid and the workspace.
+ *                  A sequence whose L_b exceeds it, or whose offsets decrease,
+ *                  gets NaN in all its o and lse entries.
+ *   k_tree, v_tree [B, T, Hkv, D] keys/values of the tree tokens.
+ *   mask           [B, T] uint64 from ltree_build_mask (bit j of row i: node j
+ *                  visible to node i).  Row i must have bit i set; a row with no
+ *                  visible tree node and L_b = 0 has no defined result.
+ *   o              [B, T, Hq, D] fp32 out.
+ *   lse            [B, Hq, T] fp32 out, natural logarithm.
+ *   workspace      >= ltree_attn_workspace_bytes(...) bytes, 256-byte aligned.
+ *                  Its contents on entry do not matter.
+ *
+ * Numerics (bf16): q.k on bf16 MFMA with fp32 accumulation; softmax in fp32;
+ * probabilities are rounded to fp16 and v converted exactly from bf16 to fp16
+ * for the fp16 MFMA P.v product with fp32 accumulation; row sums use the
+ * unrounded fp32 probabilities.  |v| must stay below the fp16 limit 65504;
+ * larger values give non-finite o.  fp32 path: fp32 throughout.
+ *
+ * Returns LTREE_OK, LTREE_ERR_INVALID_ARG, LTREE_ERR_UNSUPPORTED,
+ * LTREE_ERR_WORKSPACE or LTREE_ERR_HIP.  Two kernel launches on `stream`.
+ */
+int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+               const void* q, const void* k_prefix, const void* v_prefix,
+               const int32_t* prefix_offsets, int max_prefix_len,
+               const void* k_tree, const void* v_tree, const uint64_t* mask,
+               float* o, float* lse, void* workspace, size_t workspace_bytes,
+               hipStream_t stream);
+
+/*
+ * ltree_attn_partials -- steps 1 and 2 of ltree_attn alone (same arguments
+ * minus o and lse): writes the partial results of every prefix split and of
+ * the tree part into `workspace`.  The layout is internal; the only consumer
+ * is ltree_attn_merge called with the same sizes.  One kernel launch.
+ */
+int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
+                        float scale, const void* q, const void* k_prefix,
+                        const void* v_prefix, const int32_t* prefix_offsets,
+                        int max_prefix_len, const void* k_tree, const void* v_tree,
+                        const uint64_t* mask, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ltree_attn_merge -- step 3 of ltree_attn alone: the log-sum-exp merge
+ * (gist.science section 2 part C, "Aggregation") of the partials that
+ * ltree_attn_partials left in `workspace` into o [B,T,Hq,D] and lse [B,Hq,T].
+ * Sizes must equal those of the ltree_attn_partials call.  One kernel launch.
+ */
+int ltree_attn_merge(int B, int T, int Hq, int Hkv, int D,
+                     const int32_t* prefix_offsets, int max_prefix_len,
+                     float* o, float* lse, const void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LTREE_H */

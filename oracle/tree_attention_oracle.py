@@ -203,16 +203,19 @@ def oracle_attn_rows(q, k_prefix, v_prefix, offsets, k_tree, v_tree, parent,
     o = np.empty((len(rows), D))
     lse = np.empty(len(rows))
     vt = _f64(v_tree)
+    cache = {}  # fp64 copies of one (sequence, KV head) key/value list
     for n, (b, h, i) in enumerate(rows):
         g = h // G
-        kpg = _f64(k_prefix[int(off[b]):int(off[b + 1]), g, :])
-        vpg = _f64(v_prefix[int(off[b]):int(off[b + 1]), g, :])
-        keys = np.concatenate([kpg, kt[b, :, g, :]])
-        vals = np.concatenate([vpg, vt[b, :, g, :]])
-        L = kpg.shape[0]
+        if (b, g) not in cache:
+            cache.clear()
+            kpg = _f64(k_prefix[int(off[b]):int(off[b + 1]), g, :])
+            vpg = _f64(v_prefix[int(off[b]):int(off[b + 1]), g, :])
+            cache[(b, g)] = (np.concatenate([kpg, kt[b, :, g, :]]),
+                             np.concatenate([vpg, vt[b, :, g, :]]), kpg.shape[0])
+        keys, vals, L = cache[(b, g)]
         visible = np.ones((1, L + T), dtype=bool)
         visible[0, L:] = anc[b, i]
-        s = scale * (_f64(q[b, i, h, :])[None, :] @ keys.T)
+        s = scale * (q[b, i, h, :][None, :] @ keys.T)
         on, ln = _masked_softmax_rows(s, visible, vals)
         o[n], lse[n] = on[0], ln[0]
     return o, lse

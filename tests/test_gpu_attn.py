@@ -1,0 +1,195 @@
+"""Steps a2-a4 on the GPU, through the C ABI, against the fp64 oracle.
+
+Small cases (the oracle finishes in seconds) cover several key tiles, ragged
+split tails, every row-tile count of the MFMA kernel, D = 64 and 128, bf16
+and fp32, empty prefixes, forests, single-node trees and a merge over more
+partials than a wavefront has lanes.  Full workload sizes are checked on
+sampled rows, which the oracle computes one by one, and on properties that
+hold at any size."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import (LSE_TOL, check_parity, oracle_full, run_library, say, to_device)
+from workloads import CONFIGS, make_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # name: (B, T, Hq, Hkv, D, prefix_lens, trees, dtype)
+    "g5_t64_320rows": (1, 64, 10, 2, 128, [1000], ("bounded", 8, 3), "bf16"),
+    "g4_t64_256rows_ragged": (2, 64, 8, 2, 128, [700, 0], ("bounded", 6, 4), "bf16"),
+    "g2_t8_d64": (2, 8, 4, 2, 64, [129, 64], "uniform", "bf16"),
+    "g8_t64_two_row_blocks": (1, 64, 8, 1, 128, [300], ("bounded", 6, 4), "bf16"),
+    "single_node": (2, 1, 8, 2, 128, [257, 3], "chain", "bf16"),
+    "forest_b3": (3, 20, 6, 3, 128, [65, 0, 191], "forest", "bf16"),
+    "mha_g1_t33_d64": (1, 33, 4, 4, 64, [450], ("bounded", 5, 3), "bf16"),
+    "g3_t48_tpw3": (1, 48, 12, 4, 128, [515], ("bounded", 6, 4), "bf16"),
+    "g4_t32_tpw2_chain": (2, 32, 8, 2, 128, [900, 1300], "chain", "bf16"),
+    "fp32_d128": (2, 16, 8, 2, 128, [300, 77], "uniform", "f32"),
+    "fp32_d64_forest": (1, 9, 6, 2, 64, [40], "forest", "f32"),
+    "no_prefix_at_all": (2, 12, 4, 2, 128, [0, 0], "uniform", "bf16"),
+}
+
+
+def _small(name, seed=0):
+    B, T, Hq, Hkv, D, lens, trees, dtype = SMALL[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()) + seed)
+    return make_workload(rng, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, prefix_lens=lens, trees=trees,
+                         dtype=dtype, name=name)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_parity(name):
+    w = _small(name)
+    say("small parity", name, w.shape)
+    o, lse, mask, status = run_library(w)
+    assert int(status[0]) == 0
+    o_ref, lse_ref = oracle_full(w)
+    check_parity(w, o, lse, o_ref, lse_ref)
+
+
+def test_tiny_fp32_config():
+    w = make_config(1)
+    say("config 1 full parity")
+    o, lse, _, _ = run_library(w)
+    check_parity(w, o, lse, *oracle_full(w))
+
+
+def test_many_splits_merge(monkeypatch):
+    """64-key splits: 79 prefix partials per row, more than one per lane."""
+    monkeypatch.setenv("LTREE_SPLIT_KEYS", "64")
+    rng = np.random.default_rng(3)
+    w = make_workload(rng, B=1, T=16, Hq=8, Hkv=2, D=128, prefix_lens=[5000],
+                      trees=("bounded", 4, 3), dtype="bf16")
+    say("many splits")
+    o, lse, _, _ = run_library(w)
+    check_parity(w, o, lse, *oracle_full(w))
+
+
+def test_outlier_rows_small():
+    """The 1%-outlier recipe at a small size: softmax range stress."""
+    rng = np.random.default_rng(4)
+    w = make_workload(rng, B=1, T=64, Hq=10, Hkv=2, D=128, prefix_lens=[3000],
+                      trees=("bounded", 8, 3), dtype="bf16", outlier_frac=0.01)
+    say("outliers small")
+    o, lse, _, _ = run_library(w)
+    check_parity(w, o, lse, *oracle_full(w))
+
+
+def test_grid_larger_than_lengths():
+    """max_prefix_len above every L_b: the extra splits are empty."""
+    import tree_attention_amd as ta
+    w = _small("g4_t64_256rows_ragged")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    say("oversized max_prefix_len")
+    o, lse = ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 9000, d["k_tree"],
+                     d["v_tree"], mask, w.scale)
+    torch.cuda.synchronize()
+    check_parity(w, o.cpu(), lse.cpu(), *oracle_full(w))
+
+
+def test_deterministic():
+    import tree_attention_amd as ta
+    w = _small("g5_t64_320rows")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    say("determinism")
+    runs = [ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 1000, d["k_tree"],
+                    d["v_tree"], mask, w.scale) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o, lse in runs[1:]:
+        assert torch.equal(o, runs[0][0]) and torch.equal(lse, runs[0][1])
+
+
+def test_partials_then_merge_equals_attn():
+    import tree_attention_amd as ta
+    w = _small("forest_b3")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    ws = ta.workspace_for(d["q"], d["k_tree"], 191)
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    say("partials + merge")
+    assert ta.ltree_attn_partials(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 191,
+                                  d["k_tree"], d["v_tree"], mask, ws, w.scale) == 0
+    assert ta.ltree_attn_merge(B, T, Hq, Hkv, D, d["offsets"], 191, o, lse, ws) == 0
+    o2, lse2 = ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 191, d["k_tree"],
+                       d["v_tree"], mask, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
+def test_prefix_length_over_max_gives_nan():
+    import tree_attention_amd as ta
+    w = _small("forest_b3")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    say("L_b over max_prefix_len")
+    # sequence 2 has L = 191 > 150: its rows become NaN, the others stay exact
+    o, lse = ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 150, d["k_tree"],
+                     d["v_tree"], mask, w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu(), lse.cpu()
+    assert torch.isnan(o[2]).all() and torch.isnan(lse[2]).all()
+    o_ref, lse_ref = oracle_full(w)
+    assert np.max(np.abs(o[:2].double().numpy() - o_ref[:2])) <= 2e-2
+    assert np.max(np.abs(lse[:2].double().numpy() - lse_ref[:2])) <= LSE_TOL
+
+
+def test_error_paths_with_real_tensors():
+    import tree_attention_amd as ta
+    w = _small("g2_t8_d64")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    B, T, Hq, D = w.q.shape
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device="cuda")
+    small_ws = torch.empty((256,), dtype=torch.uint8, device="cuda")
+    st = ta.ltree_attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 129, d["k_tree"],
+                       d["v_tree"], mask, o, lse, small_ws, w.scale)
+    assert st == ta.LTREE_ERR_WORKSPACE
+    ws = ta.workspace_for(d["q"], d["k_tree"], 129)
+    assert ta.ltree_attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 129, d["k_tree"],
+                         d["v_tree"], mask, o, lse, ws, -1.0) == ta.LTREE_ERR_INVALID_ARG
+    with pytest.raises(ta.LTreeError):
+        ta.build_mask(torch.zeros((2, 65), dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------ full sizes
+
+def _sample_rows(w, n, seed):
+    B, T, Hq, _ = w.q.shape
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0, 0), (B - 1, Hq - 1, T - 1), (0, Hq - 1, 0), (B - 1, 0, T - 1)}
+    while len(rows) < n:
+        rows.add((int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(T))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_full_config_sampled_rows(k):
+    w = make_config(k)
+    say("full config", k, w.shape)
+    o, lse, mask, status = run_library(w)
+    assert int(status[0]) == 0
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    rows = _sample_rows(w, 48, k)
+    ro, rl = oracle.oracle_attn_rows(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(), w.k_tree,
+                                     w.v_tree, w.parent.numpy(), w.scale, rows)
+    eo = max(np.max(np.abs(o[b, i, h].double().numpy() - ro[n])) for n, (b, h, i) in enumerate(rows))
+    el = max(abs(float(lse[b, h, i]) - rl[n]) for n, (b, h, i) in enumerate(rows))
+    say(f"config {k}: sampled o err {eo:.3e}, lse err {el:.3e}")
+    assert eo <= 2e-2 and el <= LSE_TOL
+    # any-size property: o is a convex combination of visible values, so each
+    # feature lies within the min/max of that KV head's values
+    vmax = max(w.v_prefix.float().abs().max().item(), w.v_tree.float().abs().max().item())
+    assert o.abs().max().item() <= vmax * (1 + 1e-3)

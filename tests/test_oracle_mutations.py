@@ -31,7 +31,7 @@ MUTATIONS = {
     "parent_allows_self": ("if not (-1 <= int(p[b, i]) <= i - 1):", "if not (-1 <= int(p[b, i]) <= i):"),
     "merge_unnormalised": ("o = sum((w[k] / z)[..., None]", "o = sum((w[k])[..., None]"),
     "merge_lse_no_max": ("lse = m + np.log(z)\n", "lse = np.log(z)\n"),
-    "rows_wrong_head": ("        g = h // G\n        kpg", "        g = h % Hkv\n        kpg"),
+    "rows_wrong_head": ("        g = h // G\n        if (b, g) not in cache:", "        g = h % Hkv\n        if (b, g) not in cache:"),
 }
 
 

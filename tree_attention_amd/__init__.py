@@ -1,0 +1,30 @@
+"""Hybrid tree-verification attention for AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libltree.so`` (HIP kernels behind the C ABI of
+``include/ltree.h``); this package is its thin Python binding.  Importing the
+package loads the library and raises if it is not built.
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIBRARY_PATH,
+    LTREE_BF16,
+    LTREE_ERR_HIP,
+    LTREE_ERR_INVALID_ARG,
+    LTREE_ERR_UNSUPPORTED,
+    LTREE_ERR_WORKSPACE,
+    LTREE_F32,
+    LTREE_MAX_TREE,
+    LTREE_OK,
+    LTreeError,
+    attn,
+    build_mask,
+    ltree_attn,
+    ltree_attn_merge,
+    ltree_attn_partials,
+    ltree_attn_workspace_bytes,
+    ltree_build_mask,
+    ltree_status_string,
+    ltree_version,
+    workspace_for,
+)

@@ -1,0 +1,215 @@
+"""ctypes binding of libltree (include/ltree.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libltree.so.  PyTorch supplies device memory and the stream.  The
+functions named like the C entry points take torch tensors in the layouts the
+header states and return the C status code; ``build_mask`` and ``attn``
+allocate their outputs with torch and raise ``LTreeError`` on a bad status.
+
+There is no fallback: if libltree.so is missing or cannot be loaded, importing
+this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libltree.so")
+
+LTREE_OK = 0
+LTREE_ERR_INVALID_ARG = -1
+LTREE_ERR_UNSUPPORTED = -2
+LTREE_ERR_WORKSPACE = -3
+LTREE_ERR_HIP = -4
+LTREE_F32 = 0
+LTREE_BF16 = 1
+LTREE_MAX_TREE = 64
+
+EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
+            "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
+            "ltree_attn_merge")
+
+
+class LTreeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {ltree_status_string(status)} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m tree_attention_amd.build` "
+            "(hipcc, gfx950) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "ltree_version": (I, []),
+        "ltree_status_string": (ctypes.c_char_p, [I]),
+        "ltree_build_mask": (I, [P, I, I, P, P, P]),
+        "ltree_attn_workspace_bytes": (S, [I, I, I, I, I, I]),
+        "ltree_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, P, P, S, P]),
+        "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
+        "ltree_attn_merge": (I, [I, I, I, I, I, P, I, P, P, P, S, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+_lib = _load()
+LIBRARY_PATH = _LIB_PATH
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return LTREE_BF16
+    if t.dtype == torch.float32:
+        return LTREE_F32
+    raise ValueError(f"unsupported input dtype {t.dtype}")
+
+
+# ------------------------------------------------------------ C entry points
+
+def ltree_version() -> int:
+    return _lib.ltree_version()
+
+
+def ltree_status_string(status: int) -> str:
+    return _lib.ltree_status_string(int(status)).decode()
+
+
+def ltree_build_mask(parent, mask, status=None, stream=None) -> int:
+    """parent int32 [B, T] -> mask int64 [B, T] (uint64 bits); status int32 [1]."""
+    _dev(parent, "parent", torch.int32)
+    _dev(mask, "mask", torch.int64)
+    _dev(status, "status", torch.int32)
+    B, T = parent.shape
+    if mask.shape != (B, T):
+        raise ValueError("mask must be [B, T]")
+    return _lib.ltree_build_mask(_ptr(parent), B, T, _ptr(mask), _ptr(status), _stream(stream))
+
+
+def ltree_attn_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len) -> int:
+    return int(_lib.ltree_attn_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len))
+
+
+def _check_attn_inputs(q, k_prefix, v_prefix, prefix_offsets, k_tree, v_tree, mask):
+    dt = q.dtype
+    for name, t in (("q", q), ("k_prefix", k_prefix), ("v_prefix", v_prefix),
+                    ("k_tree", k_tree), ("v_tree", v_tree)):
+        _dev(t, name, dt)
+    _dev(prefix_offsets, "prefix_offsets", torch.int32)
+    _dev(mask, "mask", torch.int64)
+    B, T, Hq, D = q.shape
+    Hkv = k_tree.shape[2]
+    if k_tree.shape != (B, T, Hkv, D) or v_tree.shape != (B, T, Hkv, D):
+        raise ValueError("k_tree/v_tree must be [B, T, Hkv, D]")
+    if k_prefix.dim() != 3 or k_prefix.shape[1:] != (Hkv, D) or v_prefix.shape != k_prefix.shape:
+        raise ValueError("k_prefix/v_prefix must be [sum L, Hkv, D]")
+    if prefix_offsets.shape != (B + 1,) or mask.shape != (B, T):
+        raise ValueError("prefix_offsets must be [B+1] and mask [B, T]")
+    return B, T, Hq, Hkv, D
+
+
+def ltree_attn_partials(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree,
+                        mask, workspace, scale, stream=None) -> int:
+    B, T, Hq, Hkv, D = _check_attn_inputs(q, k_prefix, v_prefix, prefix_offsets, k_tree,
+                                          v_tree, mask)
+    _dev(workspace, "workspace")
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    return _lib.ltree_attn_partials(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
+        _ptr(prefix_offsets), int(max_prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def ltree_attn_merge(B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
+                     stream=None) -> int:
+    _dev(prefix_offsets, "prefix_offsets", torch.int32)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    return _lib.ltree_attn_merge(
+        B, T, Hq, Hkv, D, _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def ltree_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree, mask,
+               o, lse, workspace, scale, stream=None) -> int:
+    B, T, Hq, Hkv, D = _check_attn_inputs(q, k_prefix, v_prefix, prefix_offsets, k_tree,
+                                          v_tree, mask)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    return _lib.ltree_attn(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
+        _ptr(prefix_offsets), int(max_prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask),
+        _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
+
+
+# --------------------------------------------------- allocating conveniences
+
+def build_mask(parent, with_status=True, stream=None):
+    """Allocate and build the mask; returns (mask int64 [B, T], status int32 [1])."""
+    B, T = parent.shape
+    mask = torch.empty((B, T), dtype=torch.int64, device=parent.device)
+    status = torch.empty((1,), dtype=torch.int32, device=parent.device) if with_status else None
+    st = ltree_build_mask(parent, mask, status, stream)
+    if st != LTREE_OK:
+        raise LTreeError(st, "ltree_build_mask")
+    return mask, status
+
+
+def workspace_for(q, k_tree, max_prefix_len):
+    B, T, Hq, D = q.shape
+    n = ltree_attn_workspace_bytes(B, T, Hq, k_tree.shape[2], D, max_prefix_len)
+    if n == 0:
+        raise LTreeError(LTREE_ERR_INVALID_ARG, "ltree_attn_workspace_bytes")
+    return torch.empty((n,), dtype=torch.uint8, device=q.device)
+
+
+def attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree, mask, scale,
+         workspace=None, stream=None):
+    """Allocate o [B,T,Hq,D] fp32 and lse [B,Hq,T] fp32 and run ltree_attn."""
+    B, T, Hq, D = q.shape
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = workspace_for(q, k_tree, max_prefix_len)
+    st = ltree_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree,
+                    mask, o, lse, workspace, scale, stream)
+    if st != LTREE_OK:
+        raise LTreeError(st, "ltree_attn")
+    return o, lse

@@ -1,0 +1,136 @@
+// Partial attention with plain fp32 FMA arithmetic (steps a2 and a3), used for
+// fp32 inputs, where the contraction is tiny and precision is the point.
+//
+// gist.science page "LongSpec: Long-Context Lossless Speculative Decoding with
+// Efficient Drafting and Verification", section 2 part C: item 1 of the split
+// (cached part: prefix keys, no mask) and item 2 (speculative part: tree keys,
+// tree mask).  Each workgroup computes one partial: the softmax of its query
+// rows over one prefix split, or over the tree tokens, normalised by its own
+// sum, plus log2 of that sum.  The log-sum-exp merge joins the partials.
+//
+// Grid (Hkv, slots, B * row blocks); one query row per thread; keys are staged
+// 32 at a time in LDS as fp32 and read by every thread (broadcast reads).
+#include "ltree_internal.h"
+
+namespace ltree {
+namespace {
+
+template <typename Tin>
+__device__ inline float to_f32(Tin x);
+template <>
+__device__ inline float to_f32<float>(float x) {
+  return x;
+}
+template <>
+__device__ inline float to_f32<__bf16>(__bf16 x) {
+  return static_cast<float>(x);
+}
+
+constexpr int kKeysPerTile = 32;
+constexpr int kRowsPerWG = 256;
+
+template <typename Tin, int D>
+__global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
+  __shared__ float ks[kKeysPerTile][D + 1];
+  __shared__ float vs[kKeysPerTile][D + 1];
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int slot = blockIdx.y;
+  const int rblocks = (a.R + kRowsPerWG - 1) / kRowsPerWG;
+  const int b = blockIdx.z / rblocks;
+  const int rb = blockIdx.z % rblocks;
+  const int off0 = a.offsets[b];
+  const int L = a.offsets[b + 1] - off0;
+  const bool tree = slot == a.max_chunks;
+  const size_t kstride = static_cast<size_t>(a.Hkv) * D;
+
+  int k0, k1;
+  const Tin* kb;
+  const Tin* vb;
+  if (!tree) {
+    if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
+    k0 = slot * a.chunk;
+    if (k0 >= L) return;
+    k1 = min(k0 + a.chunk, L);
+    kb = static_cast<const Tin*>(a.kp) + (static_cast<size_t>(off0) * a.Hkv + g) * D;
+    vb = static_cast<const Tin*>(a.vp) + (static_cast<size_t>(off0) * a.Hkv + g) * D;
+  } else {
+    k0 = 0;
+    k1 = a.T;
+    kb = static_cast<const Tin*>(a.kt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
+    vb = static_cast<const Tin*>(a.vt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
+  }
+
+  const int r = rb * kRowsPerWG + tid;
+  const bool active = r < a.R;
+  const int i = active ? r / a.G : 0;
+  const int h = g * a.G + (active ? r % a.G : 0);
+  float qv[D];
+  {
+    const Tin* qp = static_cast<const Tin*>(a.q) + ((static_cast<size_t>(b) * a.T + i) * a.Hq + h) * D;
+#pragma unroll
+    for (int d = 0; d < D; ++d) qv[d] = active ? to_f32(qp[d]) * a.scale_log2 : 0.f;
+  }
+  const uint64_t mw = (tree && active) ? a.mask[static_cast<size_t>(b) * a.T + i] : ~0ull;
+
+  float m = -INFINITY, l = 0.f;
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+
+  for (int t0 = k0; t0 < k1; t0 += kKeysPerTile) {
+    __syncthreads();
+    for (int e = tid; e < kKeysPerTile * D; e += 256) {
+      const int j = e / D, d = e % D;
+      const int key = min(t0 + j, k1 - 1);
+      ks[j][d] = to_f32(kb[key * kstride + d]);
+      vs[j][d] = to_f32(vb[key * kstride + d]);
+    }
+    __syncthreads();
+    const int n = min(kKeysPerTile, k1 - t0);
+    for (int j = 0; j < n; ++j) {
+      const int key = t0 + j;
+      if (tree && !((mw >> key) & 1)) continue;
+      float s = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) s = fmaf(qv[d], ks[j][d], s);
+      const float mn = fmaxf(m, s);
+      const float alpha = exp2f(m - mn);
+      const float p = exp2f(s - mn);
+      l = fmaf(l, alpha, p);
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], alpha, p * vs[j][d]);
+      m = mn;
+    }
+  }
+
+  if (!active) return;
+  const size_t pr = (static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r;
+  const float inv = 1.f / l;
+  float* op = a.o_part + pr * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
+  a.lse_part[pr] = m + log2f(l);
+}
+
+template <typename Tin>
+hipError_t launch_typed(const Plan& p, PartialArgs a, hipStream_t stream) {
+  const int rblocks = (p.R + kRowsPerWG - 1) / kRowsPerWG;
+  const dim3 grid(p.Hkv, p.slots, p.B * rblocks);
+  if (p.D == 128) {
+    hipLaunchKernelGGL((partial_simple_kernel<Tin, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((partial_simple_kernel<Tin, 64>), grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partials_simple(ltree_dtype dtype, const Plan& p, PartialArgs a,
+                                  hipStream_t stream) {
+  return dtype == LTREE_F32 ? launch_typed<float>(p, a, stream) : launch_typed<__bf16>(p, a, stream);
+}
+
+}  // namespace ltree

@@ -1,0 +1,203 @@
+// C ABI of libltree: argument checks, work planning, kernel launches.
+// The operations are defined in include/ltree.h.
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+
+#include "ltree_internal.h"
+
+namespace ltree {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+}  // namespace
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev >= kMaxDevices) dev = kMaxDevices - 1;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    n = 256;
+  }
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) return false;
+  if (D != 64 && D != 128) return false;
+  if (T > LTREE_MAX_TREE) return false;
+  p->B = B;
+  p->T = T;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->D = D;
+  p->G = Hq / Hkv;
+  p->R = p->G * T;
+  p->max_prefix_len = max_prefix_len;
+
+  // Split size: enough prefix splits per KV head that the Hkv heads of one
+  // sequence cover every compute unit once; never below 256 keys, so that a
+  // split's partial output stays small next to the keys it reads.
+  const int cus = device_cu_count();
+  const int per_head = (cus + Hkv - 1) / Hkv;
+  long chunk = (static_cast<long>(max_prefix_len) + per_head - 1) / per_head;
+  chunk = (chunk + 63) / 64 * 64;
+  if (chunk < 256) chunk = 256;
+  if (const char* env = std::getenv("LTREE_SPLIT_KEYS")) {  // tuning sweeps only
+    const long v = std::atol(env);
+    if (v >= 64 && v % 64 == 0) chunk = v;
+  }
+  if (chunk > (1L << 30)) return false;
+  p->chunk = static_cast<int>(chunk);
+  p->max_chunks = static_cast<int>((max_prefix_len + chunk - 1) / chunk);
+  p->slots = p->max_chunks + 1;
+
+  const size_t rows = static_cast<size_t>(B) * Hkv * p->slots * p->R;
+  p->o_part_off = 0;
+  p->lse_part_off = align_up(rows * D * sizeof(float), 256);
+  p->bytes = align_up(p->lse_part_off + rows * sizeof(float), 256);
+  return true;
+}
+
+}  // namespace ltree
+
+using ltree::Plan;
+using ltree::aligned;
+
+extern "C" {
+
+int ltree_version(void) { return LTREE_VERSION; }
+
+const char* ltree_status_string(int status) {
+  switch (status) {
+    case LTREE_OK: return "ok";
+    case LTREE_ERR_INVALID_ARG: return "invalid argument";
+    case LTREE_ERR_UNSUPPORTED: return "unsupported size or dtype";
+    case LTREE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case LTREE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int ltree_build_mask(const int32_t* parent, int B, int T, uint64_t* mask, int32_t* status,
+                     hipStream_t stream) {
+  if (parent == nullptr || mask == nullptr || B < 1 || T < 1) return LTREE_ERR_INVALID_ARG;
+  if (T > LTREE_MAX_TREE) return LTREE_ERR_UNSUPPORTED;
+  if (static_cast<long>(B) * T > (1L << 30)) return LTREE_ERR_INVALID_ARG;
+  return ltree::launch_mask_build(parent, B, T, mask, status, stream) == hipSuccess
+             ? LTREE_OK
+             : LTREE_ERR_HIP;
+}
+
+size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len) {
+  Plan p;
+  return ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p) ? p.bytes : 0;
+}
+
+static int check_sizes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len) {
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (T > LTREE_MAX_TREE || (D != 64 && D != 128)) return LTREE_ERR_UNSUPPORTED;
+  // every flat index the kernels form from the query/output sizes fits in int
+  if (static_cast<long>(B) * T * Hq * D > (1L << 31) - 1) return LTREE_ERR_UNSUPPORTED;
+  return LTREE_OK;
+}
+
+int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                        const void* q, const void* k_prefix, const void* v_prefix,
+                        const int32_t* prefix_offsets, int max_prefix_len, const void* k_tree,
+                        const void* v_tree, const uint64_t* mask, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
+  const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
+  if (st != LTREE_OK) return st;
+  if (!(std::isfinite(scale) && scale > 0.f)) return LTREE_ERR_INVALID_ARG;
+  if (q == nullptr || prefix_offsets == nullptr || k_tree == nullptr || v_tree == nullptr ||
+      mask == nullptr || workspace == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (max_prefix_len > 0 && (k_prefix == nullptr || v_prefix == nullptr)) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  // 16-byte vector loads of q/k/v rows
+  if (!aligned(q, 16) || !aligned(k_tree, 16) || !aligned(v_tree, 16) ||
+      (k_prefix && !aligned(k_prefix, 16)) || (v_prefix && !aligned(v_prefix, 16))) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  Plan p;
+  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p)) return LTREE_ERR_INVALID_ARG;
+  if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
+
+  ltree::PartialArgs a{};
+  a.q = q;
+  a.kp = k_prefix;
+  a.vp = v_prefix;
+  a.offsets = prefix_offsets;
+  a.kt = k_tree;
+  a.vt = v_tree;
+  a.mask = mask;
+  a.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.o_part_off);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.lse_part_off);
+  a.B = B;
+  a.T = T;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = p.G;
+  a.R = p.R;
+  a.chunk = p.chunk;
+  a.max_chunks = p.max_chunks;
+  a.slots = p.slots;
+  a.max_prefix_len = p.max_prefix_len;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  hipError_t err;
+  if (dtype == LTREE_BF16) {
+    err = ltree::launch_partials_mfma(p, a, stream);
+  } else {
+    err = ltree::launch_partials_simple(dtype, p, a, stream);
+  }
+  return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
+}
+
+int ltree_attn_merge(int B, int T, int Hq, int Hkv, int D, const int32_t* prefix_offsets,
+                     int max_prefix_len, float* o, float* lse, const void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
+  if (st != LTREE_OK) return st;
+  if (prefix_offsets == nullptr || o == nullptr || lse == nullptr || workspace == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  Plan p;
+  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p)) return LTREE_ERR_INVALID_ARG;
+  if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
+  const char* ws = static_cast<const char*>(workspace);
+  const hipError_t err = ltree::launch_merge(
+      p, prefix_offsets, reinterpret_cast<const float*>(ws + p.o_part_off),
+      reinterpret_cast<const float*>(ws + p.lse_part_off), o, lse, stream);
+  return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
+}
+
+int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+               const void* q, const void* k_prefix, const void* v_prefix,
+               const int32_t* prefix_offsets, int max_prefix_len, const void* k_tree,
+               const void* v_tree, const uint64_t* mask, float* o, float* lse, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  if (o == nullptr || lse == nullptr) return LTREE_ERR_INVALID_ARG;
+  int st = ltree_attn_partials(dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix,
+                               prefix_offsets, max_prefix_len, k_tree, v_tree, mask, workspace,
+                               workspace_bytes, stream);
+  if (st != LTREE_OK) return st;
+  return ltree_attn_merge(B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
+                          workspace_bytes, stream);
+}
+
+}  // extern "C"

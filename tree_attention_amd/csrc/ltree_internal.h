@@ -1,0 +1,66 @@
+// Internal declarations shared by the host API and the kernel files of libltree.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ltree.h"
+
+namespace ltree {
+
+// How one ltree_attn call is cut into work.  Derived only from the sizes and
+// the device's compute-unit count, so the workspace size query and the calls
+// that use the workspace always agree.
+struct Plan {
+  int B, T, Hq, Hkv, D, G, R;  // R = G*T query rows per (sequence, KV head)
+  int max_prefix_len;
+  int chunk;       // prefix keys per split (multiple of 64)
+  int max_chunks;  // ceil(max_prefix_len / chunk): prefix splits per (b, g)
+  int slots;       // max_chunks + 1; slot max_chunks holds the tree partial
+  size_t o_part_off, lse_part_off, bytes;  // workspace layout
+};
+
+// Returns false when the sizes are invalid (the caller reports the status).
+bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// Arguments of the partial-attention kernels (steps 1 and 2).
+//
+// Workspace layout, written by the partial kernels and read by the merge:
+//   o_part  [B][Hkv][slots][R][D] fp32, each partial normalised by its own sum
+//   lse_part[B][Hkv][slots][R]    fp32, log2 of the partial's sum of
+//                                 2^(scale*log2(e)*score), i.e. lse / ln 2
+// Row r of (b, g) is tree node i = r / G of query head g*G + r % G.
+struct PartialArgs {
+  const void* q;
+  const void* kp;
+  const void* vp;
+  const int32_t* offsets;
+  const void* kt;
+  const void* vt;
+  const uint64_t* mask;
+  float* o_part;
+  float* lse_part;
+  int B, T, Hq, Hkv, G, R;
+  int chunk, max_chunks, slots, max_prefix_len;
+  int rows_per_wg, row_blocks;
+  float scale_log2;  // scale * log2(e)
+};
+
+hipError_t launch_mask_build(const int32_t* parent, int B, int T, uint64_t* mask,
+                             int32_t* status, hipStream_t stream);
+
+// bf16 inputs, D in {64, 128}: MFMA kernel.
+hipError_t launch_partials_mfma(const Plan& plan, PartialArgs args, hipStream_t stream);
+
+// fp32 inputs (or any dtype, for checking): fp32 FMA kernel.
+hipError_t launch_partials_simple(ltree_dtype dtype, const Plan& plan, PartialArgs args,
+                                  hipStream_t stream);
+
+hipError_t launch_merge(const Plan& plan, const int32_t* offsets, const float* o_part,
+                        const float* lse_part, float* o, float* lse, hipStream_t stream);
+
+}  // namespace ltree
