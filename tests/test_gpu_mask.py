@@ -34,7 +34,7 @@ def test_mask_configs(k):
 @pytest.mark.parametrize("T", [1, 2, 3, 7, 31, 32, 33, 63, 64])
 def test_mask_random_trees(T):
     rng = np.random.default_rng(T)
-    kinds = ["chain", "star", "uniform", "forest", ("bounded", 4, 3)]
+    kinds = ["chain", "star", "uniform", "forest", ("bounded", 6, 3)]
     parent = np.stack([make_tree(rng, T, kinds[b % len(kinds)]) for b in range(37)])
     say("mask random T", T)
     got, st = _build(parent)
