@@ -55,7 +55,10 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
     const long v = std::atol(env);
     if (v >= 64 && v % 64 == 0) chunk = v;
   }
-  if (chunk > (1L << 30)) return false;
+  // keys of one split are addressed with 32-bit element offsets
+  const long cap = ((1L << 31) - 1) / (static_cast<long>(Hkv) * D) / 64 * 64;
+  if (chunk > cap) chunk = cap;
+  if (chunk < 64) return false;
   p->chunk = static_cast<int>(chunk);
   p->max_chunks = static_cast<int>((max_prefix_len + chunk - 1) / chunk);
   p->slots = p->max_chunks + 1;
