@@ -235,8 +235,8 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   wait_vmem_all();
   vstore(0);
   if (ntiles > 1) {
-    kdma(1);
     vload(1);
+    kdma(1);
   }
   __syncthreads();
 
@@ -244,8 +244,9 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const char* kl = x.kl0 + ((jb >> 1) % kStages) * C::KBUF;
     const char* vl = x.vl0 + ((jb >> 1) % kStages) * C::VBUF;
 
-    // S^T = K . Q^T for keys jb*32 .. +31
-    f32x4 s[2][NT];
+    // S^T = K . Q^T for keys jb*32 .. +31: all eight K operands are read
+    // first so their LDS latency overlaps, then the MFMAs
+    bf16x8 ka[2][C::DC];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int key = (jb & 1) * 32 + 8 * (l16 >> 2) + 4 * sub + (l16 & 3);
@@ -253,14 +254,32 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       const int sw = kswz<D>(key);
 #pragma unroll
       for (int c = 0; c < C::DC; ++c) {
-        const bf16x8 A = *reinterpret_cast<const bf16x8*>(krow + (((c * 4 + grp) ^ sw) << 4));
+        ka[sub][c] = *reinterpret_cast<const bf16x8*>(krow + (((c * 4 + grp) ^ sw) << 4));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 s[2][NT];
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
           s[sub][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              A, qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub][rt], 0, 0, 0);
+              ka[sub][c], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub][rt], 0, 0, 0);
         }
       }
     }
+    // the V^T operands of this block's P.V, read now, used after the softmax
+    f16x8 va[C::DT];
+    {
+      const int chunk = (jb & 1) * 4 + grp;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        va[dt] = *reinterpret_cast<const f16x8*>(vl + vt_off(dt * 16 + l16, chunk));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
     // keys past the end of the partial, and tree keys outside the row's branch
     const int key0 = jb * 32;
@@ -331,13 +350,12 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     }
 
     // O^T += V^T . P^T
-    const int chunk = (jb & 1) * 4 + grp;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const f16x8 A = *reinterpret_cast<const f16x8*>(vl + vt_off(dt * 16 + l16, chunk));
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb[rt], acc[dt][rt], 0, 0, 0);
+        acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pb[rt], acc[dt][rt], 0, 0, 0);
       }
     }
 
@@ -350,8 +368,10 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         wait_vmem_all();  // this thread's K DMA of tile t+1 has landed
         __syncthreads();
         if (t + 2 < ntiles) {
-          kdma(t + 2);
+          // V loads first: the compiler waits for outstanding loads before
+          // reusing their registers, and at this point none are outstanding
           vload(t + 2);
+          kdma(t + 2);
         }
       }
     }

@@ -10,99 +10,114 @@
 //   M = max_s l_s,  w_s = 2^(l_s - M),  Z = sum_s w_s,
 //   o = sum_s (w_s / Z) o_s,  lse = ln 2 * (M + log2 Z).
 //
-// One wavefront per output row (b, h, i).  Lanes first scan the partial lse
-// values (max, then sum), then read the partial outputs one split at a time in
-// a fixed order, so the result is bitwise deterministic.  Each lane owns D/64
-// consecutive features, so every partial row is one coalesced 4*D-byte read.
+// Each output row (b, h, i) is served by NSG groups of D/4 lanes; a lane owns
+// four consecutive features, so every partial row is one coalesced read of 16
+// bytes per lane.  Each group first scans all partial lse values (max, then
+// sum), then accumulates its share of the partial outputs (splits q, q+NSG,
+// ...) in a fixed order; the groups' sums are added in LDS in a fixed order,
+// so the result is bitwise deterministic.  Splitting the partials over groups
+// keeps several times more loads in flight than one group per row would.
 #include "ltree_internal.h"
 
 namespace ltree {
 namespace {
 
-__device__ inline float wave_max(float v) {
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int LPR>
+__device__ inline float group_max(float v) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  for (int s = LPR / 2; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
   return v;
 }
 
-__device__ inline float wave_sum(float v) {
+template <int LPR>
+__device__ inline float group_sum(float v) {
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
+  for (int s = LPR / 2; s >= 1; s >>= 1) v += __shfl_xor(v, s);
   return v;
 }
+
+constexpr int kMergeThreads = 256;
+constexpr int kSplitGroups = 4;  // lane groups sharing one output row
 
 template <int D>
-__global__ __launch_bounds__(256) void lse_merge_kernel(
+__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
     const int32_t* __restrict__ offsets, const float* __restrict__ o_part,
     const float* __restrict__ lse_part, float* __restrict__ o, float* __restrict__ lse, int B,
     int T, int Hq, int Hkv, int G, int R, int chunk, int max_chunks, int slots,
     int max_prefix_len) {
-  constexpr int E = D / 64;  // features per lane
-  const int lane = threadIdx.x & 63;
-  const long row = static_cast<long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= static_cast<long>(B) * Hq * T) return;
-  // rows are ordered (b, h, i) so the lse writes [B, Hq, T] are contiguous
-  const int i = static_cast<int>(row % T);
-  const int h = static_cast<int>((row / T) % Hq);
-  const int b = static_cast<int>(row / (static_cast<long>(T) * Hq));
-  const int g = h / G;
-  const int r = i * G + (h % G);
+  constexpr int LPR = D / 4;                             // lanes per group
+  constexpr int NSG = kSplitGroups;
+  constexpr int RPB = kMergeThreads / (LPR * NSG);       // rows per workgroup
+  __shared__ f32x4 red[NSG - 1][RPB][LPR];
 
-  float* orow = o + ((static_cast<size_t>(b) * T + i) * Hq + h) * D + lane * E;
+  const int j = threadIdx.x % LPR;                       // lane within the group
+  const int q = (threadIdx.x / LPR) % NSG;               // split group
+  const int rl = threadIdx.x / (LPR * NSG);              // row within the workgroup
+  // rows are ordered (b, h, i) so the lse writes [B, Hq, T] are contiguous;
+  // B * Hq * T < 2^31 is checked by the host
+  const unsigned row = blockIdx.x * RPB + rl;
+  const unsigned nrows = static_cast<unsigned>(B) * Hq * T;
+  const bool valid = row < nrows;
+  const unsigned i = valid ? row % T : 0;
+  const unsigned bh = valid ? row / T : 0;
+  const unsigned h = bh % Hq;
+  const unsigned b = bh / Hq;
+  const unsigned g = h / G;
+  const unsigned r = i * G + (h % G);
+
   const int L = offsets[b + 1] - offsets[b];
-  if (L < 0 || L > max_prefix_len) {
-    // The prefix-length table disagrees with max_prefix_len: fail loudly.
-#pragma unroll
-    for (int e = 0; e < E; ++e) orow[e] = __builtin_nanf("");
-    if (lane == 0) lse[(static_cast<size_t>(b) * Hq + h) * T + i] = __builtin_nanf("");
-    return;
-  }
-  const int npre = (L + chunk - 1) / chunk;
+  const bool bad = L < 0 || L > max_prefix_len;
+  const int npre = bad ? 0 : (L + chunk - 1) / chunk;
   const int nparts = npre + 1;  // prefix splits, then the tree partial
   const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
-  auto slot_of = [&](int s) { return s < npre ? s : max_chunks; };
+  auto part_row = [&](int s) { return (base + (s < npre ? s : max_chunks)) * R + r; };
 
   float mx = -INFINITY;
-  for (int s = lane; s < nparts; s += 64) mx = fmaxf(mx, lse_part[(base + slot_of(s)) * R + r]);
-  mx = wave_max(mx);
+  for (int s = j; s < nparts; s += LPR) mx = fmaxf(mx, lse_part[part_row(s)]);
+  mx = group_max<LPR>(mx);
   float z = 0.f;
-  for (int s = lane; s < nparts; s += 64) z += exp2f(lse_part[(base + slot_of(s)) * R + r] - mx);
-  z = wave_sum(z);
+  for (int s = j; s < nparts; s += LPR) z += exp2f(lse_part[part_row(s)] - mx);
+  z = group_sum<LPR>(z);
   const float inv_z = 1.f / z;
 
-  float acc[E];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int U = 4;  // partials in flight per lane and step
+  int s = q;
+  for (; s + (U - 1) * NSG < nparts; s += U * NSG) {
+    float w[U];
+    f32x4 v[U];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  int s = 0;
-  // four partials in flight per step
-  for (; s + 4 <= nparts; s += 4) {
-    float w[4];
-    float v[4][E];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const size_t pr = (base + slot_of(s + u)) * R + r;
-      w[u] = exp2f(lse_part[pr] - mx) * inv_z;
-      const float* src = o_part + pr * D + lane * E;
-#pragma unroll
-      for (int e = 0; e < E; ++e) v[u][e] = src[e];
+    for (int u = 0; u < U; ++u) {
+      const size_t pr = part_row(s + u * NSG);
+      w[u] = lse_part[pr];
+      v[u] = reinterpret_cast<const f32x4*>(o_part + pr * D)[j];
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = fmaf(w[u], v[u][e], acc[e]);
+    for (int u = 0; u < U; ++u) acc += (exp2f(w[u] - mx) * inv_z) * v[u];
   }
-  for (; s < nparts; ++s) {
-    const size_t pr = (base + slot_of(s)) * R + r;
-    const float w = exp2f(lse_part[pr] - mx) * inv_z;
-    const float* src = o_part + pr * D + lane * E;
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = fmaf(w, src[e], acc[e]);
+  for (; s < nparts; s += NSG) {
+    const size_t pr = part_row(s);
+    acc += (exp2f(lse_part[pr] - mx) * inv_z) * reinterpret_cast<const f32x4*>(o_part + pr * D)[j];
   }
+
+  if (q > 0) red[q - 1][rl][j] = acc;
+  __syncthreads();
+  if (q > 0 || !valid) return;
 #pragma unroll
-  for (int e = 0; e < E; ++e) orow[e] = acc[e];
-  if (lane == 0) {
-    lse[(static_cast<size_t>(b) * Hq + h) * T + i] = (mx + log2f(z)) * 0.6931471805599453f;
+  for (int k = 0; k < NSG - 1; ++k) acc += red[k][rl][j];
+  f32x4* orow = reinterpret_cast<f32x4*>(o + ((static_cast<size_t>(b) * T + i) * Hq + h) * D) + j;
+  float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * T + i;
+  if (bad) {
+    // The prefix-length table disagrees with max_prefix_len: fail loudly.
+    const float nan = __builtin_nanf("");
+    *orow = (f32x4){nan, nan, nan, nan};
+    if (j == 0) *lrow = nan;
+    return;
   }
+  *orow = acc;
+  if (j == 0) *lrow = (mx + log2f(z)) * 0.6931471805599453f;
 }
 
 }  // namespace
@@ -110,13 +125,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(
 hipError_t launch_merge(const Plan& p, const int32_t* offsets, const float* o_part,
                         const float* lse_part, float* o, float* lse, hipStream_t stream) {
   const long rows = static_cast<long>(p.B) * p.Hq * p.T;
-  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  const long rows_per_block = kMergeThreads / (p.D / 4 * kSplitGroups);
+  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   if (p.D == 128) {
-    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(256), 0, stream, offsets, o_part,
+    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, offsets, o_part,
                        lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G, p.R, p.chunk,
                        p.max_chunks, p.slots, p.max_prefix_len);
   } else {
-    hipLaunchKernelGGL(lse_merge_kernel<64>, grid, dim3(256), 0, stream, offsets, o_part,
+    hipLaunchKernelGGL(lse_merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, offsets, o_part,
                        lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G, p.R, p.chunk,
                        p.max_chunks, p.slots, p.max_prefix_len);
   }

@@ -34,6 +34,8 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) return false;
   if (D != 64 && D != 128) return false;
   if (T > LTREE_MAX_TREE) return false;
+  // output rows (b, h, i) are indexed with 32-bit integers in the merge
+  if (static_cast<long>(B) * Hq * T >= (1L << 31)) return false;
   p->B = B;
   p->T = T;
   p->Hq = Hq;
