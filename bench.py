@@ -120,11 +120,13 @@ def main():
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--hot", action="store_true", help="reuse one KV copy (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB buffer 5 times (calibrates HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the kernel shards by KV head or batch with no exchange; see DESIGN.md)",
+              "(the work shards by KV head or by sequence with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -136,6 +138,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = "cuda:0"
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
     spec = CONFIGS[args.config]
     log(f"generating workload {spec['name']}")
     w = make_config(args.config)
