@@ -17,89 +17,95 @@
 // Grid (Hkv, slots, B * row_blocks), 512 threads = 8 wavefronts, two per SIMD.
 // The 16-row tiles of the workgroup's rows are dealt round-robin: tile t goes
 // to wave t % 8, so with 20 tiles (G*T = 320) waves 0-3 take three and waves
-// 4-7 two, and each SIMD (waves w and w+4) carries five.  Two waves per SIMD
-// let the matrix cores run one wave's MFMAs while the other wave does its
-// softmax arithmetic, and keep each wave within 256 registers.  Consecutive
+// 4-7 two, and each SIMD (waves w and w+4) carries five.  Consecutive
 // workgroups differ in KV head first, so with 8 KV heads every head keeps to
-// one XCD (workgroups are dealt to the 8 XCDs round-robin) and its queries
-// stay in that XCD's L2.
+// one XCD (workgroups are dealt to the 8 XCDs round-robin).
 //
 // Keys arrive in 64-key tiles and are consumed in 32-key blocks.  Per block,
 // per wavefront and per 16-row tile:
-//   S^T[key][row] = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K from LDS,
+//   S^T[key][row] = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS,
 //                              B = Q^T held in registers for the whole split;
-//   online softmax in fp32 (row max over the 4 lane groups by two permlane
-//                              swaps);
-//   O^T[d][row] += V^T . P^T  v_mfma_f32_16x16x32_f16, A = V^T from LDS,
-//                              B = P^T straight from the S^T accumulators.
+//   online softmax in fp32 (lazy reference max, see below);
+//   O^T[d][row] += V^T . P^T  v_mfma_f32_16x16x32_f16, A = V^T read from the
+//                              row-major V tile by transposing LDS reads,
+//                              B = P^T (fp16) straight from the S^T
+//                              accumulators.
 // Result layout of a 16x16 MFMA: lane (g = lane/16, c = lane%16) holds rows
 // 4g..4g+3 of column c.  Reading K rows in the order key(m) = 8(m/4) + 4s +
 // m%4 for the two 16-key halves s of a block makes lane group g hold keys
 // 8g..8g+7 of the block, exactly the k-slots the P.V MFMA expects from lane
 // group g, so probabilities never move between lanes.
 //
-// LDS, three stages of one tile each:
-//   K   [64 keys][D] bf16, filled straight from memory by global_load_lds
-//       (16 bytes per lane); the 16-byte chunks of a key row are XOR-swizzled
-//       by key so the 16 rows one lane group reads together hit distinct banks.
-//   V^T [D][64 keys] fp16, 160-byte rows, 16-byte chunks XOR-swizzled by d/8;
-//       converted from bf16 in registers while staging (exact: every finite
-//       bf16 below 65504 is an fp16).
-// Loads run two tiles ahead of the tile being computed; one barrier per tile.
-#include <type_traits>
-
+// LDS: four stages of one tile each, K [64 keys][D] and V [64 keys][D] bf16,
+// both filled straight from memory by global_load_lds (16 bytes per lane), so
+// no staging registers are needed and three tiles can be in flight while one
+// is computed.  Each thread converts the V chunks it loaded from bf16 to fp16
+// in place once they have landed (exact for |v| < 65504): probabilities go
+// into the P.V product as fp16, whose rounding error (2^-11) keeps the output
+// within tolerance even where a few large values dominate a row, which bf16
+// (2^-8) does not.  The 16-byte chunks of a row are XOR-swizzled by key so the
+// rows one lane group reads together hit distinct banks (32 banks of 4
+// bytes).  One barrier per tile.
 #include "ltree_internal.h"
 
 namespace ltree {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;    // keys per LDS tile
-constexpr int kStages = 3;   // LDS tiles in flight
+constexpr int kStages = 4;   // LDS tiles: one being computed, up to three in flight
 constexpr int kWaves = 8;    // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgroup)
 
 template <int D>
 struct Cfg {
-  static constexpr int KC16 = D / 8;                    // 16-byte chunks per key row
-  static constexpr int KROW = D * 2;                    // bytes per K row in LDS
-  static constexpr int KBUF = kTile * KROW;             // bytes per K stage
-  static constexpr int VSTR = 160;                      // bytes per V^T row
-  static constexpr int VBUF = D * VSTR;                 // bytes per V^T stage
-  static constexpr int DC = D / 32;                     // d chunks of the QK MFMA
-  static constexpr int DT = D / 16;                     // d tiles of the PV MFMA
-  static constexpr int KDMA = kTile * KC16 / kThreads;  // K 16-byte DMA loads per thread
-  static constexpr int KEYS_PER_DMA = 1024 / KROW;      // keys per wave DMA instruction
-  static constexpr int VITEMS = (kTile / 2) * KC16;     // V (key pair, chunk) items per tile
-  static constexpr int SMEM = kStages * (KBUF + VBUF);
+  static constexpr int KC16 = D / 8;                   // 16-byte chunks per key row
+  static constexpr int ROW = D * 2;                    // bytes per K or V row in LDS
+  static constexpr int BUF = kTile * ROW;              // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * BUF;                // K tile, then V tile
+  static constexpr int SMEM = kStages * STAGE;
+  static constexpr int DC = D / 32;                    // d chunks of the QK MFMA
+  static constexpr int DT = D / 16;                    // d tiles of the PV MFMA
+  static constexpr int DMA = kTile * KC16 / kThreads;  // 16-byte DMA loads per thread per tensor
+  static constexpr int ROWS_PER_DMA = 1024 / ROW;      // rows per wave DMA instruction
+  static constexpr int DMA_PER_TILE = 2 * DMA;         // vmcnt events per thread per tile
 };
 
-// Chunk swizzle of a K row: the 16 rows read by one lane group in a QK step
-// are keys 8a + b (+4) with a, b in 0..3, so the swizzle uses key bits 0,1,3,4.
+// LDS has 64 banks of 4 bytes; a 16-byte read serves 16 lanes per cycle, an
+// 8-byte read 32.  The swizzles below make every operand read of the block
+// loop conflict-free under that rule.  Neither uses key bits 2 or 5, so a
+// lane's offsets hold for both 4-key halves of a 16-key step and both
+// 32-key blocks of a tile.
+//
+// K rows: the 16 lanes of one lane group read keys 8a + b (+4), a, b in 0..3,
+// at one 16-byte chunk index; the swizzle spreads them over all 64 banks.
 template <int D>
 __device__ inline int kswz(int key) {
   if constexpr (D == 128) {
     return (key & 3) | ((key >> 1) & 12);
-  } else {
-    return (key & 3) | ((key >> 1) & 4);
+  } else {  // 128-byte rows: two rows per bank line
+    return ((key >> 1) & 1) | ((key >> 2) & 2) | ((key >> 2) & 4);
   }
 }
 
-// Byte offset of the 16-byte chunk (row d, keys 8*chunk .. 8*chunk+7) of V^T.
-__device__ inline int vt_off(int d, int chunk) {
-  return d * 160 + ((chunk ^ ((d >> 3) & 7)) << 4);
-}
-
-__device__ inline uint32_t pack_f16(float lo, float hi) {
-  const f16x2 h = __builtin_convertvector((f32x2){lo, hi}, f16x2);
-  return __builtin_bit_cast(uint32_t, h);
+// V rows: a transposing read by lane groups g and g+1 covers keys 8g + 0..3
+// and 8g + 8..11, 32 bytes of each.
+template <int D>
+__device__ inline int vswz(int key) {
+  if constexpr (D == 128) {
+    return 2 * (key & 3) + 8 * ((key >> 3) & 1);
+  } else {
+    return (key & 2) | ((key >> 1) & 4);
+  }
 }
 
 // max / sum over the four lane groups (lanes l, l^16, l^32, l^48)
@@ -120,18 +126,109 @@ __device__ inline float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ inline void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// This thread's LDS DMA writes are complete except for those of the `n` most
+// recently issued tiles (the loop issues nothing else to memory).
+template <int D>
+__device__ inline void wait_dma_except(int n) {
+  static_assert(Cfg<D>::DMA_PER_TILE == 4 || Cfg<D>::DMA_PER_TILE == 2, "vmcnt table");
+  if (n >= 2) {
+    if constexpr (Cfg<D>::DMA_PER_TILE == 4) {
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    }
+  } else if (n == 1) {
+    if constexpr (Cfg<D>::DMA_PER_TILE == 4) {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    }
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// acc + lo + hi of two fp16 (the row sums)
+__device__ inline float add_f16x2(f16x2 h, float acc) {
+  const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+  return __builtin_amdgcn_fdot2(h, ones, acc, false);
+}
+
+// two fp16 from two bf16 (exact below 65504)
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t u) {
+  const f32x2 f = {__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+}
+
+// The V^T operands of one block: for each d tile two transposing LDS reads
+// (ds_read_b64_tr_b16, four 16-bit values each).  The reads are written out
+// here, with their wait, because the compiler treats the transposing-read
+// builtin as possibly reading the tiles still arriving by LDS DMA and would
+// wait for every load in flight first, which defeats the prefetch; the loop
+// orders these reads against the DMA itself (per-thread vmcnt wait plus a
+// barrier before a tile is read).
+// Lane addresses are LDS byte offsets: a[i] addresses d tile i; the second
+// read of each tile is HI_OFF bytes (4 rows) further.
+__device__ inline uint32_t lds_off(const char* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
+}
+
+template <int HI_OFF>
+__device__ inline void read_v_operands8(const uint32_t (&a)[8], u32x2 (&r)[16]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n"
+      "ds_read_b64_tr_b16 %1, %16 offset:%c24\n"
+      "ds_read_b64_tr_b16 %2, %17\n"
+      "ds_read_b64_tr_b16 %3, %17 offset:%c24\n"
+      "ds_read_b64_tr_b16 %4, %18\n"
+      "ds_read_b64_tr_b16 %5, %18 offset:%c24\n"
+      "ds_read_b64_tr_b16 %6, %19\n"
+      "ds_read_b64_tr_b16 %7, %19 offset:%c24\n"
+      "ds_read_b64_tr_b16 %8, %20\n"
+      "ds_read_b64_tr_b16 %9, %20 offset:%c24\n"
+      "ds_read_b64_tr_b16 %10, %21\n"
+      "ds_read_b64_tr_b16 %11, %21 offset:%c24\n"
+      "ds_read_b64_tr_b16 %12, %22\n"
+      "ds_read_b64_tr_b16 %13, %22 offset:%c24\n"
+      "ds_read_b64_tr_b16 %14, %23\n"
+      "ds_read_b64_tr_b16 %15, %23 offset:%c24\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
+        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
+        "i"(HI_OFF)
+      : "memory");
+}
+
+template <int HI_OFF>
+__device__ inline void read_v_operands4(const uint32_t (&a)[4], u32x2 (&r)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %8 offset:%c12\n"
+      "ds_read_b64_tr_b16 %2, %9\n"
+      "ds_read_b64_tr_b16 %3, %9 offset:%c12\n"
+      "ds_read_b64_tr_b16 %4, %10\n"
+      "ds_read_b64_tr_b16 %5, %10 offset:%c12\n"
+      "ds_read_b64_tr_b16 %6, %11\n"
+      "ds_read_b64_tr_b16 %7, %11 offset:%c12\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
+        "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(HI_OFF)
+      : "memory");
+}
 
 // Everything one workgroup shares.
 struct Ctx {
   const PartialArgs* a;
-  char* kl0;            // K stages
-  char* vl0;            // V^T stages
+  char* smem;
   const __bf16* kbase;  // first key of this partial, KV head g
   const __bf16* vbase;
   int kstride;          // elements between consecutive keys
   int nkeys;            // keys of this partial
-  int tid, lane, wave, l16, grp;
+  int lane, wave, l16, grp;
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
   bool tree;
 };
@@ -141,7 +238,7 @@ template <int D, int NT>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
-  const int lane = x.lane, l16 = x.l16, grp = x.grp, tid = x.tid, wave = x.wave;
+  const int lane = x.lane, l16 = x.l16, grp = x.grp, wave = x.wave;
   const int nkeys = x.nkeys;
   const bool tree = x.tree;
 
@@ -172,92 +269,97 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     }
   }
 
+  // Online softmax state per row, in raw score units s = q.k, relative to a
+  // reference max m of the row:
+  //   thr   m + 8/c2: a score above it would give a probability above 2^8
+  //         (-inf while the row has seen no key),
+  //   nmc   -m*c2, the exponent offset (0 while the row has seen no key),
+  //   lsum  sum of this lane's probabilities as rounded to fp16 for P.V (the
+  //         output is normalised by the same values it accumulates).
   f32x4 acc[C::DT][NT];
-  float mrow[NT], lrow[NT];
+  float thr[NT], nmc[NT], lsum[NT];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    mrow[rt] = -INFINITY;
-    lrow[rt] = 0.f;
+    thr[rt] = -INFINITY;
+    nmc[rt] = 0.f;
+    lsum[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;
+  const float t8 = 8.f / c2;
   const int ntiles = (nkeys + kTile - 1) / kTile;
   const int nblocks = (nkeys + 31) / 32;
   const int kstride = x.kstride;
 
-  // ---- staging: K straight to LDS, V through registers
-  auto kdma = [&](int t) {
-    char* kl = x.kl0 + (t % kStages) * C::KBUF;
+  // ---- per-lane LDS offsets of the MFMA operands (stage, block half, sub
+  // block and the upper d tiles are added as uniform offsets)
+  int koff[C::DC];
+  {
+    const int key = 8 * (l16 >> 2) + (l16 & 3);  // block-relative key of sub 0
+    const int sw = kswz<D>(key);                  // the same for key + 4 and key + 32
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) koff[c] = key * C::ROW + (((c * 4 + grp) ^ sw) << 4);
+  }
+  // V^T operand of d tile dt for lane (grp, j = l16): two transposing reads.
+  // A read hands lane j of a 16-lane group element j % 4 of the 8 bytes
+  // addressed by lane 4k + j / 4, as its element k.  So lane j addresses key
+  // 8grp + j/4 (+4 for the second read), features 16dt + 4(j%4) .. +3, and
+  // receives V[8grp + k][16dt + j] for k = 0..3 (then 4..7): the eight keys of
+  // lane group grp for feature 16dt + j, the A-operand slots of the MFMA.
+  int voff[C::DT];
+  {
+    const int key = 8 * grp + (l16 >> 2);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      voff[dt] = key * C::ROW + (((2 * dt + ((l16 & 3) >> 1)) ^ vswz<D>(key)) << 4) + 8 * (l16 & 1);
+    }
+  }
+
+  // ---- staging: K and V tiles straight to LDS
+  auto dma = [&](int t) {
+    char* st = x.smem + (t % kStages) * C::STAGE;
+    char* vst = st + Cfg<D>::BUF;
     const int last = nkeys - 1 - t * kTile;  // clamp keys past the end
 #pragma unroll
-    for (int j = 0; j < C::KDMA; ++j) {
+    for (int j = 0; j < C::DMA; ++j) {
       const int blk = j * kWaves + wave;  // 1 KB block of this wave instruction
-      const int key = blk * C::KEYS_PER_DMA + lane / C::KC16;
+      const int row = blk * C::ROWS_PER_DMA + lane / C::KC16;
       const int slotc = lane % C::KC16;
-      const int kk = min(key, last);
-      const __bf16* src = x.kbase + (t * kTile + kk) * kstride + ((slotc ^ kswz<D>(key)) * 8);
-      __builtin_amdgcn_global_load_lds(src, kl + blk * 1024, 16, 0, 0);
+      const int rr = t * kTile + min(row, last);
+      const __bf16* ksrc = x.kbase + rr * kstride + ((slotc ^ kswz<D>(row)) * 8);
+      const __bf16* vsrc = x.vbase + rr * kstride + ((slotc ^ vswz<D>(row)) * 8);
+      __builtin_amdgcn_global_load_lds(ksrc, st + blk * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vsrc, vst + blk * 1024, 16, 0, 0);
     }
   };
-  u32x4 vreg[2];
-  const bool vitem = tid < C::VITEMS;
-  const int vcc = tid % C::KC16;  // d chunk of this thread's V item
-  const int vp = tid / C::KC16;   // key pair of this thread's V item
-  auto vload = [&](int t) {
-    if (vitem) {
-      const int last = nkeys - 1 - t * kTile;
-      const __bf16* src = x.vbase + (t * kTile) * kstride + vcc * 8;
-      vreg[0] = *reinterpret_cast<const u32x4*>(src + min(2 * vp, last) * kstride);
-      vreg[1] = *reinterpret_cast<const u32x4*>(src + min(2 * vp + 1, last) * kstride);
-    }
-  };
-  auto vstore = [&](int t) {
-    if (vitem) {
-      char* vl = x.vl0 + (t % kStages) * C::VBUF;
+
+  // V chunks this thread loaded into tile t's stage: bf16 -> fp16 in place
+  auto convert = [&](int t) {
+    char* vst = x.smem + (t % kStages) * C::STAGE + C::BUF;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t u0 = vreg[0][w];  // v[2p][8cc+2w], v[2p][8cc+2w+1]
-        const uint32_t u1 = vreg[1][w];  // v[2p+1][...]
-        const float x0 = __uint_as_float(u0 << 16), x1 = __uint_as_float(u0 & 0xffff0000u);
-        const float y0 = __uint_as_float(u1 << 16), y1 = __uint_as_float(u1 & 0xffff0000u);
-        const int d = 8 * vcc + 2 * w;
-        // key pair p sits at dword p%4 of 16-byte chunk p/4
-        *reinterpret_cast<uint32_t*>(vl + vt_off(d, vp >> 2) + (vp & 3) * 4) = pack_f16(x0, y0);
-        *reinterpret_cast<uint32_t*>(vl + vt_off(d + 1, vp >> 2) + (vp & 3) * 4) = pack_f16(x1, y1);
-      }
+    for (int j = 0; j < C::DMA; ++j) {
+      u32x4* p = reinterpret_cast<u32x4*>(vst + (j * kWaves + wave) * 1024 + 16 * lane);
+      const u32x4 u = *p;
+      *p = (u32x4){bf16x2_to_f16x2(u[0]), bf16x2_to_f16x2(u[1]), bf16x2_to_f16x2(u[2]),
+                   bf16x2_to_f16x2(u[3])};
     }
   };
 
-  // ---- prologue: tiles 0 and 1 in flight, tile 0 ready
-  kdma(0);
-  vload(0);
-  wait_vmem_all();
-  vstore(0);
-  if (ntiles > 1) {
-    vload(1);
-    kdma(1);
-  }
-  __syncthreads();
+  // ---- one 32-key block
+  auto block = [&](int jb) {
+    const char* kl = x.smem + ((jb >> 1) % kStages) * C::STAGE + (jb & 1) * 32 * C::ROW;
+    const char* vl = kl + C::BUF;
 
-  for (int jb = 0; jb < nblocks; ++jb) {
-    const char* kl = x.kl0 + ((jb >> 1) % kStages) * C::KBUF;
-    const char* vl = x.vl0 + ((jb >> 1) % kStages) * C::VBUF;
-
-    // S^T = K . Q^T for keys jb*32 .. +31: all eight K operands are read
-    // first so their LDS latency overlaps, then the MFMAs
+    // S^T = K . Q^T for keys jb*32 .. +31
     bf16x8 ka[2][C::DC];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int key = (jb & 1) * 32 + 8 * (l16 >> 2) + 4 * sub + (l16 & 3);
-      const char* krow = kl + key * C::KROW;
-      const int sw = kswz<D>(key);
+    for (int c = 0; c < C::DC; ++c) {
 #pragma unroll
-      for (int c = 0; c < C::DC; ++c) {
-        ka[sub][c] = *reinterpret_cast<const bf16x8*>(krow + (((c * 4 + grp) ^ sw) << 4));
+      for (int sub = 0; sub < 2; ++sub) {
+        ka[sub][c] = *reinterpret_cast<const bf16x8*>(kl + sub * 4 * C::ROW + koff[c]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
     f32x4 s[2][NT];
 #pragma unroll
     for (int c = 0; c < C::DC; ++c) {
@@ -270,16 +372,33 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         }
       }
     }
-    // the V^T operands of this block's P.V, read now, used after the softmax
+    // the V^T operands of this block's P.V, read while the QK MFMAs run,
+    // used after the softmax
+    __builtin_amdgcn_sched_barrier(0);
     f16x8 va[C::DT];
     {
-      const int chunk = (jb & 1) * 4 + grp;
+      const uint32_t vb = lds_off(vl);
+      if constexpr (C::DT == 8) {
+        const uint32_t ad[8] = {vb + voff[0], vb + voff[1], vb + voff[2], vb + voff[3],
+                                vb + voff[4], vb + voff[5], vb + voff[6], vb + voff[7]};
+        u32x2 r[16];
+        read_v_operands8<4 * C::ROW>(ad, r);
 #pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        va[dt] = *reinterpret_cast<const f16x8*>(vl + vt_off(dt * 16 + l16, chunk));
+        for (int dt = 0; dt < 8; ++dt) {
+          va[dt] = __builtin_bit_cast(f16x8, (u32x4){r[2 * dt][0], r[2 * dt][1], r[2 * dt + 1][0],
+                                                     r[2 * dt + 1][1]});
+        }
+      } else {
+        const uint32_t ad[4] = {vb + voff[0], vb + voff[1], vb + voff[2], vb + voff[3]};
+        u32x2 r[8];
+        read_v_operands4<4 * C::ROW>(ad, r);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          va[dt] = __builtin_bit_cast(f16x8, (u32x4){r[2 * dt][0], r[2 * dt][1], r[2 * dt + 1][0],
+                                                     r[2 * dt + 1][1]});
+        }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
 
     // keys past the end of the partial, and tree keys outside the row's branch
     const int key0 = jb * 32;
@@ -297,60 +416,72 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         }
     }
 
-    // Online softmax in base 2 on scores scaled by c2 = scale*log2(e).  The
-    // running max moves only when a row's block max exceeds it by more than
-    // 8/c2, i.e. when a probability would exceed 2^8; otherwise probabilities
-    // up to 2^8 are kept against the stale max (exact: the final normalisation
-    // and the lse use that same max) and the accumulator is not rescaled.
-    float mt[NT];
+    // Online softmax in base 2, with a lazily moved reference max.  Each lane
+    // checks its own eight scores against the row threshold; only when some
+    // score would give a probability above 2^8 does the wave reduce the row
+    // maxima across lane groups, move the reference and rescale.  Keeping
+    // probabilities up to 2^8 against a stale reference is exact: the final
+    // normalisation and the lse use the same reference.
+    float lm[NT];
     bool need = false;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       const float m0 = fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), s[0][rt][2]);
       const float m1 = fmaxf(fmaxf(s[0][rt][3], s[1][rt][0]), s[1][rt][1]);
-      const float m2 = fmaxf(fmaxf(s[1][rt][2], s[1][rt][3]), m0);
-      mt[rt] = group_max(fmaxf(m1, m2));
-      need = need || (mt[rt] - mrow[rt]) * c2 > 8.f;
+      lm[rt] = fmaxf(fmaxf(s[1][rt][2], s[1][rt][3]), fmaxf(m0, m1));
+      need = need || lm[rt] > thr[rt];
     }
-    if (__any(need)) {
-      // Rare.  The scaled accumulator goes back through an MFMA (0*0 + C) so
-      // that every definition of acc inside the loop is an MFMA result and acc
+    if (__builtin_expect(__any(need), 0)) {
+      // The scaled accumulator goes back through an MFMA (0*0 + C) so that
+      // every definition of acc inside the loop is an MFMA result and acc
       // stays in the accumulation registers.
       const f16x8 z8 = __builtin_bit_cast(f16x8, (u32x4){0u, 0u, 0u, 0u});
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        const float mn = fmaxf(mrow[rt], mt[rt]);
-        // a tree row can have no visible key yet (a forest): keep it empty
-        const float alpha = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((mrow[rt] - mn) * c2);
-        mrow[rt] = mn;
-        lrow[rt] *= alpha;
+        const float mt = group_max(lm[rt]);
+        const bool up = mt > thr[rt];  // this row's reference moves to mt
+        if (__any(up)) {
+          const float n_new = up ? -mt * c2 : nmc[rt];
+          // nothing accumulated yet (thr = -inf): scale by 0, never by inf
+          const float alpha = !up ? 1.f
+                              : thr[rt] == -INFINITY ? 0.f
+                                                     : __builtin_amdgcn_exp2f(n_new - nmc[rt]);
+          thr[rt] = up ? mt + t8 : thr[rt];
+          nmc[rt] = n_new;
+          lsum[rt] *= alpha;
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
+          for (int dt = 0; dt < C::DT; ++dt) {
+            acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
+          }
         }
       }
     }
 
-    // p = 2^(s*c2 - m*c2), row sums from the fp32 p, fp16 pack for P.V
+    // p = 2^(s*c2 - m*c2) in fp16 for P.V; the row sums add the same fp16
+    // values (dot product with ones, fp32 accumulation)
     f16x8 pb[NT];
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      const float mc = mrow[rt] == -INFINITY ? 0.f : mrow[rt] * c2;  // then every s is -inf
       float p[8];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          p[4 * sub + v] = __builtin_amdgcn_exp2f(fmaf(s[sub][rt][v], c2, -mc));
+          p[4 * sub + v] = __builtin_amdgcn_exp2f(fmaf(s[sub][rt][v], c2, nmc[rt]));
         }
-      lrow[rt] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      const u32x4 w = (u32x4){pack_f16(p[0], p[1]), pack_f16(p[2], p[3]), pack_f16(p[4], p[5]),
-                              pack_f16(p[6], p[7])};
-      pb[rt] = __builtin_bit_cast(f16x8, w);
+      f16x2 h[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
+        lsum[rt] = add_f16x2(h[k], lsum[rt]);
+      }
+      pb[rt] = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, h[0]),
+                                                  __builtin_bit_cast(uint32_t, h[1]),
+                                                  __builtin_bit_cast(uint32_t, h[2]),
+                                                  __builtin_bit_cast(uint32_t, h[3])});
     }
 
     // O^T += V^T . P^T
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
@@ -358,22 +489,23 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pb[rt], acc[dt][rt], 0, 0, 0);
       }
     }
+  };
 
-    // After the first block of tile t: stage V^T of tile t+1, barrier (tile
-    // t+1 is then complete in LDS), start the loads of tile t+2.
-    if ((jb & 1) == 0) {
-      const int t = jb >> 1;
-      if (t + 1 < ntiles) {
-        vstore(t + 1);
-        wait_vmem_all();  // this thread's K DMA of tile t+1 has landed
-        __syncthreads();
-        if (t + 2 < ntiles) {
-          // V loads first: the compiler waits for outstanding loads before
-          // reusing their registers, and at this point none are outstanding
-          vload(t + 2);
-          kdma(t + 2);
-        }
-      }
+  // ---- tiles 0..2 in flight.  Per tile: barrier (tile t converted by every
+  // thread; the stage of tile t-1 free), refill that stage with tile t+3,
+  // compute tile t, then wait for this thread's loads of tile t+1 and convert
+  // them.
+  for (int t = 0; t < min(3, ntiles); ++t) dma(t);
+  wait_dma_except<D>(min(2, ntiles - 1));
+  convert(0);
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();
+    if (t + 3 < ntiles) dma(t + 3);
+    block(2 * t);
+    if (2 * t + 1 < nblocks) block(2 * t + 1);
+    if (t + 1 < ntiles) {
+      wait_dma_except<D>(min(2, ntiles - 2 - t));
+      convert(t + 1);
     }
   }
 
@@ -381,7 +513,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   const size_t pbase = (static_cast<size_t>(x.b * a.Hkv + x.g) * a.slots + x.slot) * a.R;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    const float l = group_sum(lrow[rt]);
+    const float l = group_sum(lsum[rt]);
     const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
     if (r < x.rend) {
       const float inv = 1.f / l;
@@ -390,7 +522,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       for (int dt = 0; dt < C::DT; ++dt) {
         *reinterpret_cast<f32x4*>(op + dt * 16) = acc[dt][rt] * inv;
       }
-      if (grp == 0) a.lse_part[pbase + r] = mrow[rt] * c2 + __builtin_amdgcn_logf(l);
+      if (grp == 0) a.lse_part[pbase + r] = -nmc[rt] + __builtin_amdgcn_logf(l);
     }
   }
 }
@@ -398,15 +530,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
 template <int D, int TPW>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(16))) char smem[C::SMEM];
+  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
 
   Ctx x;
   x.a = &a;
-  x.kl0 = smem;
-  x.vl0 = smem + kStages * C::KBUF;
-  x.tid = threadIdx.x;
-  x.lane = x.tid & 63;
-  x.wave = x.tid >> 6;
+  x.smem = smem;
+  x.lane = threadIdx.x & 63;
+  x.wave = threadIdx.x >> 6;
   x.l16 = x.lane & 15;
   x.grp = x.lane >> 4;
   x.g = blockIdx.x;
