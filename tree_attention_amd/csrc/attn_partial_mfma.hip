@@ -26,9 +26,8 @@
 //   S^T[key][row] = K . Q^T   v_mfma_f32_16x16x32_bf16, A = K rows from LDS,
 //                              B = Q^T held in registers for the whole split;
 //   online softmax in fp32 (lazy reference max, see below);
-//   O^T[d][row] += V^T . P^T  v_mfma_f32_16x16x32_f16, A = V^T read from the
-//                              row-major V tile by transposing LDS reads,
-//                              B = P^T (fp16) straight from the S^T
+//   O^T[d][row] += V^T . P^T  v_mfma_f32_16x16x32_f16, A = V^T (fp16) from
+//                              LDS, B = P^T (fp16) straight from the S^T
 //                              accumulators.
 // Result layout of a 16x16 MFMA: lane (g = lane/16, c = lane%16) holds rows
 // 4g..4g+3 of column c.  Reading K rows in the order key(m) = 8(m/4) + 4s +
@@ -36,16 +35,17 @@
 // 8g..8g+7 of the block, exactly the k-slots the P.V MFMA expects from lane
 // group g, so probabilities never move between lanes.
 //
-// LDS: four stages of one tile each, K [64 keys][D] and V [64 keys][D] bf16,
+// LDS.  Three stages of one tile each hold K [64 keys][D] and the raw V tile,
 // both filled straight from memory by global_load_lds (16 bytes per lane), so
-// no staging registers are needed and three tiles can be in flight while one
-// is computed.  Each thread converts the V chunks it loaded from bf16 to fp16
-// in place once they have landed (exact for |v| < 65504): probabilities go
-// into the P.V product as fp16, whose rounding error (2^-11) keeps the output
-// within tolerance even where a few large values dominate a row, which bf16
-// (2^-8) does not.  The 16-byte chunks of a row are XOR-swizzled by key so the
-// rows one lane group reads together hit distinct banks (32 banks of 4
-// bytes).  One barrier per tile.
+// no staging registers are needed and two tiles can be in flight while one is
+// computed.  Once a thread's V loads of the next tile have landed it converts
+// them to fp16 and writes them transposed into one of two V^T buffers
+// [D][64 keys] (exact for |v| < 65504).  Probabilities enter the P.V product
+// as fp16, whose rounding (2^-11) keeps the output within tolerance even where
+// a few large values dominate a row, which bf16 (2^-8) does not.  LDS has 64
+// banks of 4 bytes (16 lanes per cycle for 16-byte accesses, 64 for 4-byte
+// ones); the K chunk swizzle and the V^T row pitch and cell swizzle make every
+// operand read and every V^T write conflict-free.  One barrier per tile.
 #include "ltree_internal.h"
 
 namespace ltree {
@@ -56,38 +56,37 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;    // keys per LDS tile
-constexpr int kStages = 4;   // LDS tiles: one being computed, up to three in flight
+constexpr int kStages = 3;   // DMA stages: one being computed, up to two in flight
 constexpr int kWaves = 8;    // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgroup)
+constexpr int kVtRow = 144;  // bytes per V^T row: 64 fp16 keys + 16 bytes of pitch
 
 template <int D>
 struct Cfg {
-  static constexpr int KC16 = D / 8;                   // 16-byte chunks per key row
-  static constexpr int ROW = D * 2;                    // bytes per K or V row in LDS
-  static constexpr int BUF = kTile * ROW;              // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * BUF;                // K tile, then V tile
-  static constexpr int SMEM = kStages * STAGE;
-  static constexpr int DC = D / 32;                    // d chunks of the QK MFMA
-  static constexpr int DT = D / 16;                    // d tiles of the PV MFMA
-  static constexpr int DMA = kTile * KC16 / kThreads;  // 16-byte DMA loads per thread per tensor
-  static constexpr int ROWS_PER_DMA = 1024 / ROW;      // rows per wave DMA instruction
-  static constexpr int DMA_PER_TILE = 2 * DMA;         // vmcnt events per thread per tile
+  static constexpr int KC16 = D / 8;                      // 16-byte chunks per key row
+  static constexpr int ROW = D * 2;                       // bytes per K (or raw V) row
+  static constexpr int BUF = kTile * ROW;                 // bytes of one K (or raw V) tile
+  static constexpr int STAGE = 2 * BUF;                   // K tile, then raw V tile
+  static constexpr int VT = D * kVtRow;                   // bytes of one V^T buffer
+  static constexpr int SMEM = kStages * STAGE + 2 * VT;
+  static constexpr int DC = D / 32;                       // d chunks of the QK MFMA
+  static constexpr int DT = D / 16;                       // d tiles of the PV MFMA
+  static constexpr int KDMA = kTile * KC16 / kThreads;    // K 16-byte DMA loads per thread
+  static constexpr int ROWS_PER_DMA = 1024 / ROW;         // K rows per wave DMA instruction
+  static constexpr int VITEMS = (kTile / 2) * KC16;       // V items: (key pair, d chunk)
+  static constexpr int VWAVES = VITEMS / 64;              // waves that stage V
+  static constexpr int DPT_V = KDMA + 2;                  // DMA per tile, V-staging waves
+  static constexpr int DPT_K = KDMA;                      // DMA per tile, other waves
 };
 
-// LDS has 64 banks of 4 bytes; a 16-byte read serves 16 lanes per cycle, an
-// 8-byte read 32.  The swizzles below make every operand read of the block
-// loop conflict-free under that rule.  Neither uses key bits 2 or 5, so a
-// lane's offsets hold for both 4-key halves of a 16-key step and both
-// 32-key blocks of a tile.
-//
 // K rows: the 16 lanes of one lane group read keys 8a + b (+4), a, b in 0..3,
-// at one 16-byte chunk index; the swizzle spreads them over all 64 banks.
+// at one 16-byte chunk index; the swizzle spreads them over all 64 banks.  It
+// does not use key bits 2 or 5, so a lane's offsets hold for both 4-key halves
+// of a 16-key step and both 32-key blocks of a tile.
 template <int D>
 __device__ inline int kswz(int key) {
   if constexpr (D == 128) {
@@ -97,16 +96,11 @@ __device__ inline int kswz(int key) {
   }
 }
 
-// V rows: a transposing read by lane groups g and g+1 covers keys 8g + 0..3
-// and 8g + 8..11, 32 bytes of each.
-template <int D>
-__device__ inline int vswz(int key) {
-  if constexpr (D == 128) {
-    return 2 * (key & 3) + 8 * ((key >> 3) & 1);
-  } else {
-    return (key & 2) | ((key >> 1) & 4);
-  }
-}
+// V^T: row d at d * kVtRow, its 16-byte cell q (keys 8q..8q+7) at position
+// q ^ ((d / 16) % 8).  With the 144-byte pitch the 16 rows one lane group reads
+// (a d tile) hit distinct bank groups, and the XOR spreads the cells the
+// staging threads write together (features 8c + e for 16 values of c).
+__device__ inline int vt_off(int d, int q) { return d * kVtRow + ((q ^ ((d >> 4) & 7)) << 4); }
 
 // max / sum over the four lane groups (lanes l, l^16, l^32, l^48)
 __device__ inline float group_max(float x) {
@@ -126,22 +120,21 @@ __device__ inline float group_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// This thread's LDS DMA writes are complete except for those of the `n` most
-// recently issued tiles (the loop issues nothing else to memory).
-template <int D>
+// This thread's LDS DMA writes are complete except for those of the `n` (0..1)
+// most recently issued tiles, DPT loads per tile (the loop issues nothing
+// else to memory).
+template <int DPT>
 __device__ inline void wait_dma_except(int n) {
-  static_assert(Cfg<D>::DMA_PER_TILE == 4 || Cfg<D>::DMA_PER_TILE == 2, "vmcnt table");
-  if (n >= 2) {
-    if constexpr (Cfg<D>::DMA_PER_TILE == 4) {
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    } else {
+  static_assert(DPT >= 1 && DPT <= 4, "vmcnt table");
+  if (n >= 1) {
+    if constexpr (DPT == 4) {
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    }
-  } else if (n == 1) {
-    if constexpr (Cfg<D>::DMA_PER_TILE == 4) {
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else {
+    } else if constexpr (DPT == 3) {
+      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+    } else if constexpr (DPT == 2) {
       asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
     }
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -154,70 +147,12 @@ __device__ inline float add_f16x2(f16x2 h, float acc) {
   return __builtin_amdgcn_fdot2(h, ones, acc, false);
 }
 
-// two fp16 from two bf16 (exact below 65504)
-__device__ inline uint32_t bf16x2_to_f16x2(uint32_t u) {
-  const f32x2 f = {__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u)};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
-}
-
-// The V^T operands of one block: for each d tile two transposing LDS reads
-// (ds_read_b64_tr_b16, four 16-bit values each).  The reads are written out
-// here, with their wait, because the compiler treats the transposing-read
-// builtin as possibly reading the tiles still arriving by LDS DMA and would
-// wait for every load in flight first, which defeats the prefetch; the loop
-// orders these reads against the DMA itself (per-thread vmcnt wait plus a
-// barrier before a tile is read).
-// Lane addresses are LDS byte offsets: a[i] addresses d tile i; the second
-// read of each tile is HI_OFF bytes (4 rows) further.
-__device__ inline uint32_t lds_off(const char* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)(p)));
-}
-
-template <int HI_OFF>
-__device__ inline void read_v_operands8(const uint32_t (&a)[8], u32x2 (&r)[16]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %16\n"
-      "ds_read_b64_tr_b16 %1, %16 offset:%c24\n"
-      "ds_read_b64_tr_b16 %2, %17\n"
-      "ds_read_b64_tr_b16 %3, %17 offset:%c24\n"
-      "ds_read_b64_tr_b16 %4, %18\n"
-      "ds_read_b64_tr_b16 %5, %18 offset:%c24\n"
-      "ds_read_b64_tr_b16 %6, %19\n"
-      "ds_read_b64_tr_b16 %7, %19 offset:%c24\n"
-      "ds_read_b64_tr_b16 %8, %20\n"
-      "ds_read_b64_tr_b16 %9, %20 offset:%c24\n"
-      "ds_read_b64_tr_b16 %10, %21\n"
-      "ds_read_b64_tr_b16 %11, %21 offset:%c24\n"
-      "ds_read_b64_tr_b16 %12, %22\n"
-      "ds_read_b64_tr_b16 %13, %22 offset:%c24\n"
-      "ds_read_b64_tr_b16 %14, %23\n"
-      "ds_read_b64_tr_b16 %15, %23 offset:%c24\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7]), "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11]),
-        "=&v"(r[12]), "=&v"(r[13]), "=&v"(r[14]), "=&v"(r[15])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7]),
-        "i"(HI_OFF)
-      : "memory");
-}
-
-template <int HI_OFF>
-__device__ inline void read_v_operands4(const uint32_t (&a)[4], u32x2 (&r)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8\n"
-      "ds_read_b64_tr_b16 %1, %8 offset:%c12\n"
-      "ds_read_b64_tr_b16 %2, %9\n"
-      "ds_read_b64_tr_b16 %3, %9 offset:%c12\n"
-      "ds_read_b64_tr_b16 %4, %10\n"
-      "ds_read_b64_tr_b16 %5, %10 offset:%c12\n"
-      "ds_read_b64_tr_b16 %6, %11\n"
-      "ds_read_b64_tr_b16 %7, %11 offset:%c12\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "i"(HI_OFF)
-      : "memory");
+// fp16 pair (lo, hi) from the low halves (hi = false) or high halves of two
+// bf16 pairs (exact below 65504)
+__device__ inline uint32_t pack_f16_of_bf16(uint32_t lo, uint32_t hi, bool upper) {
+  const float a = __uint_as_float(upper ? (lo & 0xffff0000u) : (lo << 16));
+  const float b = __uint_as_float(upper ? (hi & 0xffff0000u) : (hi << 16));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
 }
 
 // Everything one workgroup shares.
@@ -228,7 +163,7 @@ struct Ctx {
   const __bf16* vbase;
   int kstride;          // elements between consecutive keys
   int nkeys;            // keys of this partial
-  int lane, wave, l16, grp;
+  int tid, lane, wave, l16, grp;
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
   bool tree;
 };
@@ -238,7 +173,7 @@ template <int D, int NT>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
-  const int lane = x.lane, l16 = x.l16, grp = x.grp, wave = x.wave;
+  const int lane = x.lane, l16 = x.l16, grp = x.grp, wave = x.wave, tid = x.tid;
   const int nkeys = x.nkeys;
   const bool tree = x.tree;
 
@@ -291,9 +226,10 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   const int ntiles = (nkeys + kTile - 1) / kTile;
   const int nblocks = (nkeys + 31) / 32;
   const int kstride = x.kstride;
+  char* const vt0 = x.smem + kStages * C::STAGE;  // V^T buffers 0 and 1
 
   // ---- per-lane LDS offsets of the MFMA operands (stage, block half, sub
-  // block and the upper d tiles are added as uniform offsets)
+  // block and V^T buffer are added as uniform offsets)
   int koff[C::DC];
   {
     const int key = 8 * (l16 >> 2) + (l16 & 3);  // block-relative key of sub 0
@@ -301,55 +237,62 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
 #pragma unroll
     for (int c = 0; c < C::DC; ++c) koff[c] = key * C::ROW + (((c * 4 + grp) ^ sw) << 4);
   }
-  // V^T operand of d tile dt for lane (grp, j = l16): two transposing reads.
-  // A read hands lane j of a 16-lane group element j % 4 of the 8 bytes
-  // addressed by lane 4k + j / 4, as its element k.  So lane j addresses key
-  // 8grp + j/4 (+4 for the second read), features 16dt + 4(j%4) .. +3, and
-  // receives V[8grp + k][16dt + j] for k = 0..3 (then 4..7): the eight keys of
-  // lane group grp for feature 16dt + j, the A-operand slots of the MFMA.
-  int voff[C::DT];
-  {
-    const int key = 8 * grp + (l16 >> 2);
+  // V^T operand of d tile dt for lane (grp, l16): row 16dt + l16, cell
+  // 4h + grp for block half h; the XOR term of cell 4h + grp in a row of
+  // d tile dt is ((4h + grp) ^ dt), whose bit 2 is uniform.
+  int voff[4];
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      voff[dt] = key * C::ROW + (((2 * dt + ((l16 & 3) >> 1)) ^ vswz<D>(key)) << 4) + 8 * (l16 & 1);
-    }
-  }
+  for (int d4 = 0; d4 < 4; ++d4) voff[d4] = l16 * kVtRow + (((grp ^ d4) & 3) << 4);
 
-  // ---- staging: K and V tiles straight to LDS
+  // ---- staging
+  // K: 16-byte chunks straight to the K tile, swizzled by key.
+  // V: item (key pair m, d chunk c) of thread tid < VITEMS: keys 2m and 2m+1
+  // of chunk c land in two 1 KB slots of the raw V tile at this lane's
+  // position, so only this thread reads them back.
+  const bool vstage = wave < C::VWAVES;
+  const int vm = tid / C::KC16, vc = tid % C::KC16;
   auto dma = [&](int t) {
     char* st = x.smem + (t % kStages) * C::STAGE;
-    char* vst = st + Cfg<D>::BUF;
     const int last = nkeys - 1 - t * kTile;  // clamp keys past the end
 #pragma unroll
-    for (int j = 0; j < C::DMA; ++j) {
+    for (int j = 0; j < C::KDMA; ++j) {
       const int blk = j * kWaves + wave;  // 1 KB block of this wave instruction
       const int row = blk * C::ROWS_PER_DMA + lane / C::KC16;
       const int slotc = lane % C::KC16;
-      const int rr = t * kTile + min(row, last);
-      const __bf16* ksrc = x.kbase + rr * kstride + ((slotc ^ kswz<D>(row)) * 8);
-      const __bf16* vsrc = x.vbase + rr * kstride + ((slotc ^ vswz<D>(row)) * 8);
+      const __bf16* ksrc = x.kbase + (t * kTile + min(row, last)) * kstride + ((slotc ^ kswz<D>(row)) * 8);
       __builtin_amdgcn_global_load_lds(ksrc, st + blk * 1024, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vsrc, vst + blk * 1024, 16, 0, 0);
+    }
+    if (vstage) {
+      char* vst = st + Cfg<D>::BUF;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const __bf16* vsrc = x.vbase + (t * kTile + min(2 * vm + j, last)) * kstride + vc * 8;
+        char* vdst = vst + (j * Cfg<D>::VWAVES + wave) * 1024;
+        __builtin_amdgcn_global_load_lds(vsrc, vdst, 16, 0, 0);
+      }
     }
   };
-
-  // V chunks this thread loaded into tile t's stage: bf16 -> fp16 in place
+  // This thread's V item of tile t, bf16 -> fp16, transposed into V^T buffer
+  // t % 2: for each feature d = 8c + e, the dword (key 2m, key 2m+1).
   auto convert = [&](int t) {
-    char* vst = x.smem + (t % kStages) * C::STAGE + C::BUF;
+    if (vstage) {
+      const char* vst = x.smem + (t % kStages) * C::STAGE + C::BUF;
+      const u32x4 u0 = *reinterpret_cast<const u32x4*>(vst + wave * 1024 + 16 * lane);
+      const u32x4 u1 = *reinterpret_cast<const u32x4*>(vst + (C::VWAVES + wave) * 1024 + 16 * lane);
+      char* vt = vt0 + (t & 1) * C::VT + 4 * (vm & 3);
 #pragma unroll
-    for (int j = 0; j < C::DMA; ++j) {
-      u32x4* p = reinterpret_cast<u32x4*>(vst + (j * kWaves + wave) * 1024 + 16 * lane);
-      const u32x4 u = *p;
-      *p = (u32x4){bf16x2_to_f16x2(u[0]), bf16x2_to_f16x2(u[1]), bf16x2_to_f16x2(u[2]),
-                   bf16x2_to_f16x2(u[3])};
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = pack_f16_of_bf16(u0[e >> 1], u1[e >> 1], e & 1);
+        *reinterpret_cast<uint32_t*>(vt + vt_off(8 * vc + e, vm >> 2)) = w;
+      }
     }
   };
 
   // ---- one 32-key block
   auto block = [&](int jb) {
-    const char* kl = x.smem + ((jb >> 1) % kStages) * C::STAGE + (jb & 1) * 32 * C::ROW;
-    const char* vl = kl + C::BUF;
+    const int h = jb & 1;
+    const char* kl = x.smem + ((jb >> 1) % kStages) * C::STAGE + h * 32 * C::ROW;
+    const char* vl = vt0 + ((jb >> 1) & 1) * C::VT;
 
     // S^T = K . Q^T for keys jb*32 .. +31
     bf16x8 ka[2][C::DC];
@@ -372,32 +315,12 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         }
       }
     }
-    // the V^T operands of this block's P.V, read while the QK MFMAs run,
-    // used after the softmax
-    __builtin_amdgcn_sched_barrier(0);
+    // the V^T operands of this block's P.V (rows 16dt + l16, cell 4h + grp)
     f16x8 va[C::DT];
-    {
-      const uint32_t vb = lds_off(vl);
-      if constexpr (C::DT == 8) {
-        const uint32_t ad[8] = {vb + voff[0], vb + voff[1], vb + voff[2], vb + voff[3],
-                                vb + voff[4], vb + voff[5], vb + voff[6], vb + voff[7]};
-        u32x2 r[16];
-        read_v_operands8<4 * C::ROW>(ad, r);
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          va[dt] = __builtin_bit_cast(f16x8, (u32x4){r[2 * dt][0], r[2 * dt][1], r[2 * dt + 1][0],
-                                                     r[2 * dt + 1][1]});
-        }
-      } else {
-        const uint32_t ad[4] = {vb + voff[0], vb + voff[1], vb + voff[2], vb + voff[3]};
-        u32x2 r[8];
-        read_v_operands4<4 * C::ROW>(ad, r);
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          va[dt] = __builtin_bit_cast(f16x8, (u32x4){r[2 * dt][0], r[2 * dt][1], r[2 * dt + 1][0],
-                                                     r[2 * dt + 1][1]});
-        }
-      }
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int uni = dt * 16 * kVtRow + ((((4 * h) ^ dt) & 4) << 4);
+      va[dt] = *reinterpret_cast<const f16x8*>(vl + uni + voff[dt & 3]);
     }
 
     // keys past the end of the partial, and tree keys outside the row's branch
@@ -410,7 +333,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
           const bool in = key0 + 8 * grp + 4 * sub + v < nkeys;
 #pragma unroll
           for (int rt = 0; rt < NT; ++rt) {
-            const uint32_t bits = (jb & 1) ? (vbits[rt] >> 8) : vbits[rt];
+            const uint32_t bits = h ? (vbits[rt] >> 8) : vbits[rt];
             if (!(in && ((bits >> (4 * sub + v)) & 1u))) s[sub][rt][v] = -INFINITY;
           }
         }
@@ -469,16 +392,16 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         for (int v = 0; v < 4; ++v) {
           p[4 * sub + v] = __builtin_amdgcn_exp2f(fmaf(s[sub][rt][v], c2, nmc[rt]));
         }
-      f16x2 h[4];
+      f16x2 hp[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        h[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
-        lsum[rt] = add_f16x2(h[k], lsum[rt]);
+        hp[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
+        lsum[rt] = add_f16x2(hp[k], lsum[rt]);
       }
-      pb[rt] = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, h[0]),
-                                                  __builtin_bit_cast(uint32_t, h[1]),
-                                                  __builtin_bit_cast(uint32_t, h[2]),
-                                                  __builtin_bit_cast(uint32_t, h[3])});
+      pb[rt] = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, hp[0]),
+                                                 __builtin_bit_cast(uint32_t, hp[1]),
+                                                 __builtin_bit_cast(uint32_t, hp[2]),
+                                                 __builtin_bit_cast(uint32_t, hp[3])});
     }
 
     // O^T += V^T . P^T
@@ -491,20 +414,27 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     }
   };
 
-  // ---- tiles 0..2 in flight.  Per tile: barrier (tile t converted by every
-  // thread; the stage of tile t-1 free), refill that stage with tile t+3,
-  // compute tile t, then wait for this thread's loads of tile t+1 and convert
-  // them.
-  for (int t = 0; t < min(3, ntiles); ++t) dma(t);
-  wait_dma_except<D>(min(2, ntiles - 1));
+  // ---- tiles 0 and 1 in flight.  Per tile: barrier (V^T of tile t written
+  // by every thread; the DMA stage and V^T buffer of tile t-1 free), refill
+  // that stage with tile t+2, compute tile t, then wait for this thread's
+  // loads of tile t+1 and convert them.
+  auto wait_own = [&](int later) {
+    if (vstage) {
+      wait_dma_except<C::DPT_V>(later);
+    } else {
+      wait_dma_except<C::DPT_K>(later);
+    }
+  };
+  for (int t = 0; t < min(2, ntiles); ++t) dma(t);
+  wait_own(min(1, ntiles - 1));
   convert(0);
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();
-    if (t + 3 < ntiles) dma(t + 3);
+    if (t + 2 < ntiles) dma(t + 2);
     block(2 * t);
     if (2 * t + 1 < nblocks) block(2 * t + 1);
     if (t + 1 < ntiles) {
-      wait_dma_except<D>(min(2, ntiles - 2 - t));
+      wait_own(min(1, ntiles - 2 - t));
       convert(t + 1);
     }
   }
@@ -535,6 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   Ctx x;
   x.a = &a;
   x.smem = smem;
+  x.tid = threadIdx.x;
   x.lane = threadIdx.x & 63;
   x.wave = threadIdx.x >> 6;
   x.l16 = x.lane & 15;
