@@ -5,8 +5,10 @@
 // Attention"): item 1 of the split is the cached part (the long prefix KV
 // cache, no mask), item 2 the speculative part (the tree tokens, tree mask).
 // Each workgroup produces one partial softmax result: its query rows against
-// one prefix split, or against the tree tokens under the mask.  The
-// log-sum-exp merge ("Aggregation") joins the partials.
+// one prefix split; the last split of a sequence (the only one when the prefix
+// is empty) continues over the tree tokens under the mask, so no workgroup is
+// spent on the tiny tree part alone.  The log-sum-exp merge ("Aggregation")
+// joins the partials.
 //
 // Work decomposition.  All G*T query rows that read one KV head (the GQA group
 // times the tree tokens) share every key, so one workgroup takes all of them
@@ -46,6 +48,8 @@
 // banks of 4 bytes (16 lanes per cycle for 16-byte accesses, 64 for 4-byte
 // ones); the K chunk swizzle and the V^T row pitch and cell swizzle make every
 // operand read and every V^T write conflict-free.  One barrier per tile.
+#include <type_traits>
+
 #include "ltree_internal.h"
 
 namespace ltree {
@@ -59,7 +63,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;    // keys per LDS tile
-constexpr int kStages = 3;   // DMA stages: one being computed, up to two in flight
+constexpr int kStages = 3;   // LDS buffers of each kind (K, raw V, V^T); tile t uses t % 3
 constexpr int kWaves = 8;    // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgroup)
@@ -70,9 +74,12 @@ struct Cfg {
   static constexpr int KC16 = D / 8;                      // 16-byte chunks per key row
   static constexpr int ROW = D * 2;                       // bytes per K (or raw V) row
   static constexpr int BUF = kTile * ROW;                 // bytes of one K (or raw V) tile
-  static constexpr int STAGE = 2 * BUF;                   // K tile, then raw V tile
   static constexpr int VT = D * kVtRow;                   // bytes of one V^T buffer
-  static constexpr int SMEM = kStages * STAGE + 2 * VT;
+  // LDS: kStages K tiles, then kStages raw V tiles, then kStages V^T buffers
+  static constexpr int K0 = 0;
+  static constexpr int R0 = kStages * BUF;
+  static constexpr int T0 = 2 * kStages * BUF;
+  static constexpr int SMEM = T0 + kStages * VT;
   static constexpr int DC = D / 32;                       // d chunks of the QK MFMA
   static constexpr int DT = D / 16;                       // d tiles of the PV MFMA
   static constexpr int KDMA = kTile * KC16 / kThreads;    // K 16-byte DMA loads per thread
@@ -159,13 +166,15 @@ __device__ inline uint32_t pack_f16_of_bf16(uint32_t lo, uint32_t hi, bool upper
 struct Ctx {
   const PartialArgs* a;
   char* smem;
-  const __bf16* kbase;  // first key of this partial, KV head g
+  const __bf16* kbase;  // first prefix key of this partial, KV head g
   const __bf16* vbase;
+  const __bf16* ktree;  // tree key 0 of this sequence, KV head g
+  const __bf16* vtree;
   int kstride;          // elements between consecutive keys
-  int nkeys;            // keys of this partial
+  int npk;              // prefix keys of this partial
+  bool tree;            // the tree keys follow them
   int tid, lane, wave, l16, grp;
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
-  bool tree;
 };
 
 // The per-wave body: NT row tiles (rows rbase + 16*(wave + 8*rt) + l16).
@@ -174,8 +183,9 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
   const int lane = x.lane, l16 = x.l16, grp = x.grp, wave = x.wave, tid = x.tid;
-  const int nkeys = x.nkeys;
+  const int npk = x.npk;
   const bool tree = x.tree;
+  const int T = x.a->T;
 
   // ---- queries of this wave's rows, as the B operand (Q^T) of the QK MFMA
   bf16x8 qf[NT][C::DC];
@@ -223,117 +233,143 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
   const float c2 = a.scale_log2;
   const float t8 = 8.f / c2;
-  const int ntiles = (nkeys + kTile - 1) / kTile;
-  const int nblocks = (nkeys + 31) / 32;
+  // prefix tiles, then one tree tile (T <= 64)
+  const int ptiles = (npk + kTile - 1) / kTile;
+  const int ntiles = ptiles + (tree ? 1 : 0);
   const int kstride = x.kstride;
-  char* const vt0 = x.smem + kStages * C::STAGE;  // V^T buffers 0 and 1
 
-  // ---- per-lane LDS offsets of the MFMA operands (stage, block half, sub
-  // block and V^T buffer are added as uniform offsets)
+  // ---- per-lane LDS offsets of the MFMA operands.  Stage, block half, sub
+  // block, d tile and V^T buffer are compile-time and go into the 16-bit
+  // offset field of the LDS instructions; the region bases above 64 KB are
+  // folded into the lane offsets (kept opaque so the compiler does not split
+  // them back out).
   int koff[C::DC];
   {
     const int key = 8 * (l16 >> 2) + (l16 & 3);  // block-relative key of sub 0
     const int sw = kswz<D>(key);                  // the same for key + 4 and key + 32
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c) koff[c] = key * C::ROW + (((c * 4 + grp) ^ sw) << 4);
+    for (int c = 0; c < C::DC; ++c) koff[c] = C::K0 + key * C::ROW + (((c * 4 + grp) ^ sw) << 4);
   }
   // V^T operand of d tile dt for lane (grp, l16): row 16dt + l16, cell
   // 4h + grp for block half h; the XOR term of cell 4h + grp in a row of
   // d tile dt is ((4h + grp) ^ dt), whose bit 2 is uniform.
   int voff[4];
 #pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4) voff[d4] = l16 * kVtRow + (((grp ^ d4) & 3) << 4);
+  for (int d4 = 0; d4 < 4; ++d4) {
+    voff[d4] = C::T0 + l16 * kVtRow + (((grp ^ d4) & 3) << 4);
+    asm volatile("" : "+v"(voff[d4]));
+  }
 
-  // ---- staging
+  // ---- staging.  Tile t uses K tile, raw V tile and V^T buffer t % 3;
+  // every stage index below is a compile-time constant (the tile loop is
+  // unrolled by three).
   // K: 16-byte chunks straight to the K tile, swizzled by key.
   // V: item (key pair m, d chunk c) of thread tid < VITEMS: keys 2m and 2m+1
   // of chunk c land in two 1 KB slots of the raw V tile at this lane's
   // position, so only this thread reads them back.
+  char* const sm = x.smem;
   const bool vstage = wave < C::VWAVES;
   const int vm = tid / C::KC16, vc = tid % C::KC16;
-  auto dma = [&](int t) {
-    char* st = x.smem + (t % kStages) * C::STAGE;
-    const int last = nkeys - 1 - t * kTile;  // clamp keys past the end
+  // per-thread source offsets (elements) within a tile; a prefix tile further
+  // is 64 * kstride elements on
+  int ksoff[C::KDMA];
+  int krow[C::KDMA];
+#pragma unroll
+  for (int j = 0; j < C::KDMA; ++j) {
+    const int blk = j * kWaves + wave;
+    krow[j] = blk * C::ROWS_PER_DMA + lane / C::KC16;
+    const int slotc = lane % C::KC16;
+    ksoff[j] = krow[j] * kstride + ((slotc ^ kswz<D>(krow[j])) * 8);
+  }
+  const int vsoff = (2 * vm) * kstride + vc * 8;
+  const long tstep = static_cast<long>(kTile) * kstride;
+  auto dma = [&](auto S_, int t) {
+    constexpr int S = decltype(S_)::value;
+    // rows past the end of the keys repeat the last key (masked later)
+    const bool tt = t == ptiles;  // the tree tile
+    const bool full = !tt && (t + 1) * kTile <= npk;
+    const int last = tt ? T - 1 : npk - 1 - t * kTile;
+    const __bf16* kb = tt ? x.ktree : x.kbase + t * tstep;
+    const __bf16* vb = tt ? x.vtree : x.vbase + t * tstep;
 #pragma unroll
     for (int j = 0; j < C::KDMA; ++j) {
-      const int blk = j * kWaves + wave;  // 1 KB block of this wave instruction
-      const int row = blk * C::ROWS_PER_DMA + lane / C::KC16;
-      const int slotc = lane % C::KC16;
-      const __bf16* ksrc = x.kbase + (t * kTile + min(row, last)) * kstride + ((slotc ^ kswz<D>(row)) * 8);
-      __builtin_amdgcn_global_load_lds(ksrc, st + blk * 1024, 16, 0, 0);
+      const __bf16* src = full ? kb + ksoff[j] : kb + ksoff[j] + (min(krow[j], last) - krow[j]) * kstride;
+      char* dst = sm + Cfg<D>::K0 + S * Cfg<D>::BUF + (j * kWaves + wave) * 1024;
+      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     }
     if (vstage) {
-      char* vst = st + Cfg<D>::BUF;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const __bf16* vsrc = x.vbase + (t * kTile + min(2 * vm + j, last)) * kstride + vc * 8;
-        char* vdst = vst + (j * Cfg<D>::VWAVES + wave) * 1024;
-        __builtin_amdgcn_global_load_lds(vsrc, vdst, 16, 0, 0);
+        const __bf16* src = full ? vb + vsoff + j * kstride
+                                 : vb + vsoff + (min(2 * vm + j, last) - 2 * vm) * kstride;
+        char* dst = sm + Cfg<D>::R0 + S * Cfg<D>::BUF + (j * Cfg<D>::VWAVES + wave) * 1024;
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
       }
     }
   };
-  // This thread's V item of tile t, bf16 -> fp16, transposed into V^T buffer
-  // t % 2: for each feature d = 8c + e, the dword (key 2m, key 2m+1).
-  auto convert = [&](int t) {
+  // This thread's V item, bf16 -> fp16, transposed into V^T buffer S: for
+  // each feature d = 8c + e, the dword (key 2m, key 2m+1); the eight cells of
+  // a thread are 144 bytes apart (vt_off is linear in e for d = 8c + e).
+  int rdoff = C::R0 + wave * 1024 + 16 * lane;
+  int wroff = C::T0 + vt_off(8 * vc, vm >> 2) + 4 * (vm & 3);
+  asm volatile("" : "+v"(rdoff), "+v"(wroff));
+  auto convert = [&](auto S_) {
+    constexpr int S = decltype(S_)::value;
     if (vstage) {
-      const char* vst = x.smem + (t % kStages) * C::STAGE + C::BUF;
-      const u32x4 u0 = *reinterpret_cast<const u32x4*>(vst + wave * 1024 + 16 * lane);
-      const u32x4 u1 = *reinterpret_cast<const u32x4*>(vst + (C::VWAVES + wave) * 1024 + 16 * lane);
-      char* vt = vt0 + (t & 1) * C::VT + 4 * (vm & 3);
+      const char* rb = sm + rdoff + S * C::BUF;
+      const u32x4 u0 = *reinterpret_cast<const u32x4*>(rb);
+      const u32x4 u1 = *reinterpret_cast<const u32x4*>(rb + C::VWAVES * 1024);
+      char* wb = sm + wroff + S * C::VT;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = pack_f16_of_bf16(u0[e >> 1], u1[e >> 1], e & 1);
-        *reinterpret_cast<uint32_t*>(vt + vt_off(8 * vc + e, vm >> 2)) = w;
+        *reinterpret_cast<uint32_t*>(wb + e * kVtRow) = pack_f16_of_bf16(u0[e >> 1], u1[e >> 1], e & 1);
       }
     }
   };
-
-  // ---- one 32-key block
-  auto block = [&](int jb) {
-    const int h = jb & 1;
-    const char* kl = x.smem + ((jb >> 1) % kStages) * C::STAGE + h * 32 * C::ROW;
-    const char* vl = vt0 + ((jb >> 1) & 1) * C::VT;
-
-    // S^T = K . Q^T for keys jb*32 .. +31
-    bf16x8 ka[2][C::DC];
-#pragma unroll
-    for (int c = 0; c < C::DC; ++c) {
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        ka[sub][c] = *reinterpret_cast<const bf16x8*>(kl + sub * 4 * C::ROW + koff[c]);
-      }
+  auto wait_own = [&](int later) {
+    if (vstage) {
+      wait_dma_except<C::DPT_V>(later);
+    } else {
+      wait_dma_except<C::DPT_K>(later);
     }
+  };
+
+  // ---- one 32-key block: block half H of the tile in stage S, whose first
+  // `valid` keys are real (prefix or tree keys); tree blocks also apply the
+  // ancestor mask
+  auto block = [&](auto S_, auto H_, int valid, bool treeblk) {
+    constexpr int S = decltype(S_)::value;
+    constexpr int H = decltype(H_)::value;
+    // S^T = K . Q^T
     f32x4 s[2][NT];
 #pragma unroll
     for (int c = 0; c < C::DC; ++c) {
+      bf16x8 ka[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        ka[sub] = *reinterpret_cast<const bf16x8*>(sm + koff[c] + S * C::BUF + H * 32 * C::ROW +
+                                                   sub * 4 * C::ROW);
+      }
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int rt = 0; rt < NT; ++rt) {
           s[sub][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              ka[sub][c], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub][rt], 0, 0, 0);
+              ka[sub], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub][rt], 0, 0, 0);
         }
       }
     }
-    // the V^T operands of this block's P.V (rows 16dt + l16, cell 4h + grp)
-    f16x8 va[C::DT];
-#pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const int uni = dt * 16 * kVtRow + ((((4 * h) ^ dt) & 4) << 4);
-      va[dt] = *reinterpret_cast<const f16x8*>(vl + uni + voff[dt & 3]);
-    }
 
-    // keys past the end of the partial, and tree keys outside the row's branch
-    const int key0 = jb * 32;
-    if (tree || key0 + 32 > nkeys) {
+    // keys past the end, and tree keys outside the row's branch
+    if (treeblk || valid < 32) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const bool in = key0 + 8 * grp + 4 * sub + v < nkeys;
+          const bool in = 8 * grp + 4 * sub + v < valid;
 #pragma unroll
           for (int rt = 0; rt < NT; ++rt) {
-            const uint32_t bits = h ? (vbits[rt] >> 8) : vbits[rt];
+            const uint32_t bits = !treeblk ? 0xffu : H ? (vbits[rt] >> 8) : vbits[rt];
             if (!(in && ((bits >> (4 * sub + v)) & 1u))) s[sub][rt][v] = -INFINITY;
           }
         }
@@ -404,39 +440,49 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
                                                  __builtin_bit_cast(uint32_t, hp[3])});
     }
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T; V^T operand of d tile dt: rows 16dt + l16, cell
+    // 4H + grp
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
+      const int uni = S * C::VT + dt * 16 * kVtRow + ((((4 * H) ^ dt) & 4) << 4);
+      const f16x8 va = *reinterpret_cast<const f16x8*>(sm + voff[dt & 3] + uni);
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pb[rt], acc[dt][rt], 0, 0, 0);
+        acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rt], acc[dt][rt], 0, 0, 0);
       }
     }
   };
 
-  // ---- tiles 0 and 1 in flight.  Per tile: barrier (V^T of tile t written
-  // by every thread; the DMA stage and V^T buffer of tile t-1 free), refill
-  // that stage with tile t+2, compute tile t, then wait for this thread's
-  // loads of tile t+1 and convert them.
-  auto wait_own = [&](int later) {
-    if (vstage) {
-      wait_dma_except<C::DPT_V>(later);
-    } else {
-      wait_dma_except<C::DPT_K>(later);
-    }
-  };
-  for (int t = 0; t < min(2, ntiles); ++t) dma(t);
-  wait_own(min(1, ntiles - 1));
-  convert(0);
-  for (int t = 0; t < ntiles; ++t) {
+  // ---- Schedule.  Tiles 0 and 1 in flight.  Per tile t: barrier (V^T of
+  // tile t written by every thread; the buffers of tile t-1 free), load tile
+  // t+2 into them, compute tile t, then wait for this thread's loads of tile
+  // t+1 and convert them.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  auto tile = [&](auto S_, int t) {
+    constexpr int S = decltype(S_)::value;
+    using SN = std::integral_constant<int, (S + 1) % kStages>;
+    using SNN = std::integral_constant<int, (S + 2) % kStages>;
     __syncthreads();
-    if (t + 2 < ntiles) dma(t + 2);
-    block(2 * t);
-    if (2 * t + 1 < nblocks) block(2 * t + 1);
+    if (t + 2 < ntiles) dma(SNN{}, t + 2);
+    const bool tt = t == ptiles;
+    const int nk = tt ? T : min(kTile, npk - t * kTile);  // real keys of this tile
+    block(S_, I0{}, min(nk, 32), tt);
+    if (nk > 32) block(S_, I1{}, nk - 32, tt);
     if (t + 1 < ntiles) {
       wait_own(min(1, ntiles - 2 - t));
-      convert(t + 1);
+      convert(SN{});
     }
+  };
+  dma(I0{}, 0);
+  if (ntiles > 1) dma(I1{}, 1);
+  wait_own(min(1, ntiles - 1));
+  convert(I0{});
+  for (int t = 0; t < ntiles; t += kStages) {
+    tile(I0{}, t);
+    if (t + 1 < ntiles) tile(I1{}, t + 1);
+    if (t + 2 < ntiles) tile(I2{}, t + 2);
   }
 
   // ---- normalise and write the partial
@@ -477,20 +523,23 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.rbase = rb * a.rows_per_wg;
   const int off0 = a.offsets[x.b];
   const int L = a.offsets[x.b + 1] - off0;
-  x.tree = x.slot == a.max_chunks;
+  if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
+  // slot s: prefix keys [s*chunk, min((s+1)*chunk, L)); the last one (slot 0
+  // when L = 0) also the tree keys
+  const int nparts = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+  if (x.slot >= nparts) return;
+  const int k0 = x.slot * a.chunk;
+  x.npk = max(0, min(a.chunk, L - k0));
+  x.tree = x.slot == nparts - 1;
   x.kstride = a.Hkv * D;
-  if (!x.tree) {
-    if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
-    const int k0 = x.slot * a.chunk;
-    if (k0 >= L) return;
-    x.nkeys = min(a.chunk, L - k0);
-    const size_t row0 = static_cast<size_t>(off0) + k0;
-    x.kbase = static_cast<const __bf16*>(a.kp) + (row0 * a.Hkv + x.g) * D;
-    x.vbase = static_cast<const __bf16*>(a.vp) + (row0 * a.Hkv + x.g) * D;
-  } else {
-    x.nkeys = a.T;
-    x.kbase = static_cast<const __bf16*>(a.kt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
-    x.vbase = static_cast<const __bf16*>(a.vt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
+  const size_t row0 = static_cast<size_t>(off0) + k0;
+  x.kbase = static_cast<const __bf16*>(a.kp) + (row0 * a.Hkv + x.g) * D;
+  x.vbase = static_cast<const __bf16*>(a.vp) + (row0 * a.Hkv + x.g) * D;
+  x.ktree = static_cast<const __bf16*>(a.kt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
+  x.vtree = static_cast<const __bf16*>(a.vt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
+  if (x.npk == 0) {  // tree only: the prefix pointers may not be dereferenceable
+    x.kbase = x.ktree;
+    x.vbase = x.vtree;
   }
 
   // Row tiles of this workgroup and how many fall to this wave.  Every wave

@@ -9,7 +9,9 @@
 // sum, plus log2 of that sum.  The log-sum-exp merge joins the partials.
 //
 // Grid (Hkv, slots, B * row blocks); one query row per thread; keys are staged
-// 32 at a time in LDS as fp32 and read by every thread (broadcast reads).
+// 32 at a time in LDS as fp32 and read by every thread (broadcast reads).  The
+// last prefix split of a sequence (slot 0 when its prefix is empty) continues
+// over the tree keys.
 #include "ltree_internal.h"
 
 namespace ltree {
@@ -42,25 +44,19 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   const int rb = blockIdx.z % rblocks;
   const int off0 = a.offsets[b];
   const int L = a.offsets[b + 1] - off0;
-  const bool tree = slot == a.max_chunks;
+  if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
+  // slot s: prefix keys [s*chunk, min((s+1)*chunk, L)); the last one (slot 0
+  // when L = 0) also the tree keys
+  const int nparts = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+  if (slot >= nparts) return;
+  const int k0 = slot * a.chunk;
+  const int npk = max(0, min(a.chunk, L - k0));
+  const bool tree = slot == nparts - 1;
   const size_t kstride = static_cast<size_t>(a.Hkv) * D;
-
-  int k0, k1;
-  const Tin* kb;
-  const Tin* vb;
-  if (!tree) {
-    if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
-    k0 = slot * a.chunk;
-    if (k0 >= L) return;
-    k1 = min(k0 + a.chunk, L);
-    kb = static_cast<const Tin*>(a.kp) + (static_cast<size_t>(off0) * a.Hkv + g) * D;
-    vb = static_cast<const Tin*>(a.vp) + (static_cast<size_t>(off0) * a.Hkv + g) * D;
-  } else {
-    k0 = 0;
-    k1 = a.T;
-    kb = static_cast<const Tin*>(a.kt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
-    vb = static_cast<const Tin*>(a.vt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
-  }
+  const Tin* kp = static_cast<const Tin*>(a.kp) + (static_cast<size_t>(off0 + k0) * a.Hkv + g) * D;
+  const Tin* vp = static_cast<const Tin*>(a.vp) + (static_cast<size_t>(off0 + k0) * a.Hkv + g) * D;
+  const Tin* kt = static_cast<const Tin*>(a.kt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
+  const Tin* vt = static_cast<const Tin*>(a.vt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
 
   const int r = rb * kRowsPerWG + tid;
   const bool active = r < a.R;
@@ -72,26 +68,32 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) qv[d] = active ? to_f32(qp[d]) * a.scale_log2 : 0.f;
   }
-  const uint64_t mw = (tree && active) ? a.mask[static_cast<size_t>(b) * a.T + i] : ~0ull;
+  const uint64_t mw = (tree && active) ? a.mask[static_cast<size_t>(b) * a.T + i] : 0ull;
 
   float m = -INFINITY, l = 0.f;
   float acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
 
-  for (int t0 = k0; t0 < k1; t0 += kKeysPerTile) {
+  // prefix keys (tiles 0 .. ptiles-1), then the tree keys (one more pass)
+  const int ptiles = (npk + kKeysPerTile - 1) / kKeysPerTile;
+  const int ttiles = tree ? (a.T + kKeysPerTile - 1) / kKeysPerTile : 0;
+  for (int tt = 0; tt < ptiles + ttiles; ++tt) {
+    const bool intree = tt >= ptiles;
+    const int t0 = (intree ? tt - ptiles : tt) * kKeysPerTile;
+    const int n = min(kKeysPerTile, (intree ? a.T : npk) - t0);
+    const Tin* kb = intree ? kt : kp;
+    const Tin* vb = intree ? vt : vp;
     __syncthreads();
     for (int e = tid; e < kKeysPerTile * D; e += 256) {
       const int j = e / D, d = e % D;
-      const int key = min(t0 + j, k1 - 1);
+      const int key = t0 + min(j, n - 1);
       ks[j][d] = to_f32(kb[key * kstride + d]);
       vs[j][d] = to_f32(vb[key * kstride + d]);
     }
     __syncthreads();
-    const int n = min(kKeysPerTile, k1 - t0);
     for (int j = 0; j < n; ++j) {
-      const int key = t0 + j;
-      if (tree && !((mw >> key) & 1)) continue;
+      if (intree && !((mw >> (t0 + j)) & 1)) continue;
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qv[d], ks[j][d], s);
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   }
 
   if (!active) return;
-  const size_t pr = (static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r;
+  const size_t pr = (static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r;  // active row
   const float inv = 1.f / l;
   float* op = a.o_part + pr * D;
 #pragma unroll

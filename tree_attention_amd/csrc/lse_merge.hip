@@ -4,7 +4,8 @@
 // Efficient Drafting and Verification", section 2 part C, "Aggregation": the
 // partial softmax results of the cached part and of the speculative part are
 // joined exactly with a log-sum-exp step.  Here the cached part itself arrives
-// as several prefix splits, so the same merge also reduces the splits.
+// as several prefix splits (the last of which has also taken in the tree
+// keys), so the same merge reduces the splits.
 //
 // For one output row with partials (o_s, l_s), l_s = log2 of the partial sum:
 //   M = max_s l_s,  w_s = 2^(l_s - M),  Z = sum_s w_s,
@@ -69,10 +70,11 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
 
   const int L = offsets[b + 1] - offsets[b];
   const bool bad = L < 0 || L > max_prefix_len;
-  const int npre = bad ? 0 : (L + chunk - 1) / chunk;
-  const int nparts = npre + 1;  // prefix splits, then the tree partial
+  // one partial per prefix split, the last of which also covers the tree
+  // keys; one tree-only partial when the prefix is empty
+  const int nparts = bad || L == 0 ? 1 : (L + chunk - 1) / chunk;
   const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
-  auto part_row = [&](int s) { return (base + (s < npre ? s : max_chunks)) * R + r; };
+  auto part_row = [&](int s) { return (base + s) * R + r; };
 
   float mx = -INFINITY;
   for (int s = j; s < nparts; s += LPR) mx = fmaxf(mx, lse_part[part_row(s)]);

@@ -63,7 +63,9 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
   if (chunk < 64) return false;
   p->chunk = static_cast<int>(chunk);
   p->max_chunks = static_cast<int>((max_prefix_len + chunk - 1) / chunk);
-  p->slots = p->max_chunks + 1;
+  // the last split of a sequence also takes the tree keys; an empty prefix
+  // still needs one partial for them
+  p->slots = p->max_chunks > 0 ? p->max_chunks : 1;
 
   const size_t rows = static_cast<size_t>(B) * Hkv * p->slots * p->R;
   p->o_part_off = 0;

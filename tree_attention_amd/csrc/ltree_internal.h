@@ -17,7 +17,9 @@ struct Plan {
   int max_prefix_len;
   int chunk;       // prefix keys per split (multiple of 64)
   int max_chunks;  // ceil(max_prefix_len / chunk): prefix splits per (b, g)
-  int slots;       // max_chunks + 1; slot max_chunks holds the tree partial
+  int slots;       // max(max_chunks, 1).  Slot s of sequence b holds prefix
+                   // keys [s*chunk, min((s+1)*chunk, L_b)); its last
+                   // non-empty slot (slot 0 when L_b = 0) also the T tree keys
   size_t o_part_off, lse_part_off, bytes;  // workspace layout
 };
 
