@@ -93,8 +93,10 @@ int ltree_build_mask(const int32_t* parent, int B, int T, uint64_t* mask,
 /*
  * ltree_attn_workspace_bytes -- size of the scratch buffer `ltree_attn`,
  * `ltree_attn_partials` and `ltree_attn_merge` need for these sizes on the
- * current device.  The workspace holds the fp32 partial results of the prefix
- * splits and of the tree part.  Returns 0 if the sizes are invalid.
+ * current device.  The workspace holds the partial results of the prefix
+ * splits (the last split of a sequence also covers its tree tokens): fp32 for
+ * fp32 inputs; for bf16 inputs 16-bit normalised values with one fp32 scale
+ * per row.  Returns 0 if the sizes are invalid.
  */
 size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
                                   int max_prefix_len);
@@ -133,8 +135,10 @@ size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
  *
  * Numerics (bf16): q.k on bf16 MFMA with fp32 accumulation; softmax in fp32;
  * probabilities are rounded to fp16 and v converted exactly from bf16 to fp16
- * for the fp16 MFMA P.v product with fp32 accumulation; row sums use the
- * unrounded fp32 probabilities.  |v| must stay below the fp16 limit 65504;
+ * for the fp16 MFMA P.v product with fp32 accumulation; the row sums add the
+ * same fp16-rounded probabilities.  Each split's normalised output row is
+ * stored as 16-bit values relative to the row's largest magnitude (error at
+ * most 2^-16 of it) for the merge.  |v| must stay below the fp16 limit 65504;
  * larger values give non-finite o.  fp32 path: fp32 throughout.
  *
  * Returns LTREE_OK, LTREE_ERR_INVALID_ARG, LTREE_ERR_UNSUPPORTED,
@@ -164,9 +168,10 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
  * ltree_attn_merge -- step 3 of ltree_attn alone: the log-sum-exp merge
  * (gist.science section 2 part C, "Aggregation") of the partials that
  * ltree_attn_partials left in `workspace` into o [B,T,Hq,D] and lse [B,Hq,T].
- * Sizes must equal those of the ltree_attn_partials call.  One kernel launch.
+ * dtype and sizes must equal those of the ltree_attn_partials call (dtype
+ * selects the partial format).  One kernel launch.
  */
-int ltree_attn_merge(int B, int T, int Hq, int Hkv, int D,
+int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
                      const int32_t* prefix_offsets, int max_prefix_len,
                      float* o, float* lse, const void* workspace,
                      size_t workspace_bytes, hipStream_t stream);

@@ -120,7 +120,7 @@ def test_partials_then_merge_equals_attn():
     say("partials + merge")
     assert ta.ltree_attn_partials(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 191,
                                   d["k_tree"], d["v_tree"], mask, ws, w.scale) == 0
-    assert ta.ltree_attn_merge(B, T, Hq, Hkv, D, d["offsets"], 191, o, lse, ws) == 0
+    assert ta.ltree_attn_merge(d["q"].dtype, B, T, Hq, Hkv, D, d["offsets"], 191, o, lse, ws) == 0
     o2, lse2 = ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 191, d["k_tree"],
                        d["v_tree"], mask, w.scale)
     torch.cuda.synchronize()

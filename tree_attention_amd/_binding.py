@@ -53,7 +53,7 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_workspace_bytes": (S, [I, I, I, I, I, I]),
         "ltree_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, P, P, S, P]),
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
-        "ltree_attn_merge": (I, [I, I, I, I, I, P, I, P, P, P, S, P]),
+        "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -150,14 +150,18 @@ def ltree_attn_partials(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
 
 
-def ltree_attn_merge(B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
+def ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
                      stream=None) -> int:
+    """dtype: the torch dtype of the inputs given to ltree_attn_partials."""
     _dev(prefix_offsets, "prefix_offsets", torch.int32)
     _dev(o, "o", torch.float32)
     _dev(lse, "lse", torch.float32)
     _dev(workspace, "workspace")
+    code = {torch.float32: LTREE_F32, torch.bfloat16: LTREE_BF16}.get(dtype)
+    if code is None:
+        raise LTreeError(f"unsupported dtype {dtype}")
     return _lib.ltree_attn_merge(
-        B, T, Hq, Hkv, D, _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse),
+        code, B, T, Hq, Hkv, D, _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
 
 

@@ -60,6 +60,7 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 64;    // keys per LDS tile
@@ -485,20 +486,36 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     if (t + 2 < ntiles) tile(I2{}, t + 2);
   }
 
-  // ---- normalise and write the partial
+  // ---- normalise and write the partial.  A row of o = acc / l goes out as
+  // int16 snorm values acc / max|acc| with the row's max|o| as its scale
+  // (the 16-bit form halves the partials' memory traffic; its error is at most
+  // 2^-16 of the row's largest magnitude).  Row r's D features are spread
+  // over the four lane groups, so the max takes a reduction across them.
   const size_t pbase = (static_cast<size_t>(x.b * a.Hkv + x.g) * a.slots + x.slot) * a.R;
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     const float l = group_sum(lsum[rt]);
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[dt][rt][i]));
+    mx = group_max(mx);
+    const float inv = mx > 0.f ? 1.f / mx : 0.f;
     const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
     if (r < x.rend) {
-      const float inv = 1.f / l;
-      float* op = a.o_part + (pbase + r) * D + 4 * grp;
+      int16_t* op = static_cast<int16_t*>(a.o_part) + (pbase + r) * D + 4 * grp;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        *reinterpret_cast<f32x4*>(op + dt * 16) = acc[dt][rt] * inv;
+        const f32x4 v = acc[dt][rt] * inv;
+        const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(v[0], v[1]));
+        const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(v[2], v[3]));
+        *reinterpret_cast<u32x2*>(op + dt * 16) = (u32x2){lo, hi};
       }
-      if (grp == 0) a.lse_part[pbase + r] = -nmc[rt] + __builtin_amdgcn_logf(l);
+      if (grp == 0) {
+        a.lse_part[pbase + r] = -nmc[rt] + __builtin_amdgcn_logf(l);
+        a.scale_part[pbase + r] = mx / l;
+      }
     }
   }
 }

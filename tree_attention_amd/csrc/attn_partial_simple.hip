@@ -110,7 +110,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   if (!active) return;
   const size_t pr = (static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r;  // active row
   const float inv = 1.f / l;
-  float* op = a.o_part + pr * D;
+  float* op = static_cast<float*>(a.o_part) + pr * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;
   a.lse_part[pr] = m + log2f(l);

@@ -24,6 +24,7 @@ namespace ltree {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int LPR>
 __device__ inline float group_max(float v) {
@@ -42,12 +43,26 @@ __device__ inline float group_sum(float v) {
 constexpr int kMergeThreads = 256;
 constexpr int kSplitGroups = 4;  // lane groups sharing one output row
 
-template <int D>
+// Four features of partial row pr for lane j: fp32, or int16 snorm values
+// times the row's scale.
+template <int D, bool SNORM>
+__device__ inline f32x4 load_part(const void* o_part, const float* scale_part, size_t pr, int j) {
+  if constexpr (SNORM) {
+    const s16x4 q = reinterpret_cast<const s16x4*>(static_cast<const int16_t*>(o_part) + pr * D)[j];
+    const float sc = scale_part[pr] * (1.f / 32767.f);
+    return (f32x4){static_cast<float>(q[0]), static_cast<float>(q[1]), static_cast<float>(q[2]),
+                   static_cast<float>(q[3])} * sc;
+  } else {
+    return reinterpret_cast<const f32x4*>(static_cast<const float*>(o_part) + pr * D)[j];
+  }
+}
+
+template <int D, bool SNORM>
 __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
-    const int32_t* __restrict__ offsets, const float* __restrict__ o_part,
-    const float* __restrict__ lse_part, float* __restrict__ o, float* __restrict__ lse, int B,
-    int T, int Hq, int Hkv, int G, int R, int chunk, int max_chunks, int slots,
-    int max_prefix_len) {
+    const int32_t* __restrict__ offsets, const void* __restrict__ o_part,
+    const float* __restrict__ scale_part, const float* __restrict__ lse_part,
+    float* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv, int G, int R,
+    int chunk, int slots, int max_prefix_len) {
   constexpr int LPR = D / 4;                             // lanes per group
   constexpr int NSG = kSplitGroups;
   constexpr int RPB = kMergeThreads / (LPR * NSG);       // rows per workgroup
@@ -94,14 +109,14 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
     for (int u = 0; u < U; ++u) {
       const size_t pr = part_row(s + u * NSG);
       w[u] = lse_part[pr];
-      v[u] = reinterpret_cast<const f32x4*>(o_part + pr * D)[j];
+      v[u] = load_part<D, SNORM>(o_part, scale_part, pr, j);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc += (exp2f(w[u] - mx) * inv_z) * v[u];
   }
   for (; s < nparts; s += NSG) {
     const size_t pr = part_row(s);
-    acc += (exp2f(lse_part[pr] - mx) * inv_z) * reinterpret_cast<const f32x4*>(o_part + pr * D)[j];
+    acc += (exp2f(lse_part[pr] - mx) * inv_z) * load_part<D, SNORM>(o_part, scale_part, pr, j);
   }
 
   if (q > 0) red[q - 1][rl][j] = acc;
@@ -124,19 +139,33 @@ __global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
 
 }  // namespace
 
-hipError_t launch_merge(const Plan& p, const int32_t* offsets, const float* o_part,
-                        const float* lse_part, float* o, float* lse, hipStream_t stream) {
+template <int D, bool SNORM>
+void launch_typed(const Plan& p, dim3 grid, const int32_t* offsets, const void* o_part,
+                  const float* scale_part, const float* lse_part, float* o, float* lse,
+                  hipStream_t stream) {
+  hipLaunchKernelGGL((lse_merge_kernel<D, SNORM>), grid, dim3(kMergeThreads), 0, stream, offsets,
+                     o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G, p.R,
+                     p.chunk, p.slots, p.max_prefix_len);
+}
+
+hipError_t launch_merge(const Plan& p, bool snorm, const int32_t* offsets, const void* o_part,
+                        const float* scale_part, const float* lse_part, float* o, float* lse,
+                        hipStream_t stream) {
   const long rows = static_cast<long>(p.B) * p.Hq * p.T;
   const long rows_per_block = kMergeThreads / (p.D / 4 * kSplitGroups);
   const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
   if (p.D == 128) {
-    hipLaunchKernelGGL(lse_merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, offsets, o_part,
-                       lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G, p.R, p.chunk,
-                       p.max_chunks, p.slots, p.max_prefix_len);
+    if (snorm) {
+      launch_typed<128, true>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+    } else {
+      launch_typed<128, false>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+    }
   } else {
-    hipLaunchKernelGGL(lse_merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, offsets, o_part,
-                       lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G, p.R, p.chunk,
-                       p.max_chunks, p.slots, p.max_prefix_len);
+    if (snorm) {
+      launch_typed<64, true>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+    } else {
+      launch_typed<64, false>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+    }
   }
   return hipGetLastError();
 }

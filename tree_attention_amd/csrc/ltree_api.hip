@@ -69,7 +69,8 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
 
   const size_t rows = static_cast<size_t>(B) * Hkv * p->slots * p->R;
   p->o_part_off = 0;
-  p->lse_part_off = align_up(rows * D * sizeof(float), 256);
+  p->scale_part_off = align_up(rows * D * sizeof(float), 256);
+  p->lse_part_off = align_up(p->scale_part_off + rows * sizeof(float), 256);
   p->bytes = align_up(p->lse_part_off + rows * sizeof(float), 256);
   return true;
 }
@@ -152,7 +153,8 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
   a.kt = k_tree;
   a.vt = v_tree;
   a.mask = mask;
-  a.o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.o_part_off);
+  a.o_part = static_cast<char*>(workspace) + p.o_part_off;
+  a.scale_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.scale_part_off);
   a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.lse_part_off);
   a.B = B;
   a.T = T;
@@ -175,9 +177,11 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
   return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
 }
 
-int ltree_attn_merge(int B, int T, int Hq, int Hkv, int D, const int32_t* prefix_offsets,
+int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
+                     const int32_t* prefix_offsets,
                      int max_prefix_len, float* o, float* lse, const void* workspace,
                      size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
   if (prefix_offsets == nullptr || o == nullptr || lse == nullptr || workspace == nullptr) {
@@ -188,7 +192,8 @@ int ltree_attn_merge(int B, int T, int Hq, int Hkv, int D, const int32_t* prefix
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
   const char* ws = static_cast<const char*>(workspace);
   const hipError_t err = ltree::launch_merge(
-      p, prefix_offsets, reinterpret_cast<const float*>(ws + p.o_part_off),
+      p, dtype == LTREE_BF16, prefix_offsets, ws + p.o_part_off,
+      reinterpret_cast<const float*>(ws + p.scale_part_off),
       reinterpret_cast<const float*>(ws + p.lse_part_off), o, lse, stream);
   return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
 }
@@ -203,8 +208,8 @@ int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float sc
                                prefix_offsets, max_prefix_len, k_tree, v_tree, mask, workspace,
                                workspace_bytes, stream);
   if (st != LTREE_OK) return st;
-  return ltree_attn_merge(B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
-                          workspace_bytes, stream);
+  return ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse,
+                          workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,7 +20,7 @@ struct Plan {
   int slots;       // max(max_chunks, 1).  Slot s of sequence b holds prefix
                    // keys [s*chunk, min((s+1)*chunk, L_b)); its last
                    // non-empty slot (slot 0 when L_b = 0) also the T tree keys
-  size_t o_part_off, lse_part_off, bytes;  // workspace layout
+  size_t o_part_off, scale_part_off, lse_part_off, bytes;  // workspace layout
 };
 
 // Returns false when the sizes are invalid (the caller reports the status).
@@ -32,9 +32,12 @@ int device_cu_count();
 // Arguments of the partial-attention kernels (steps 1 and 2).
 //
 // Workspace layout, written by the partial kernels and read by the merge:
-//   o_part  [B][Hkv][slots][R][D] fp32, each partial normalised by its own sum
-//   lse_part[B][Hkv][slots][R]    fp32, log2 of the partial's sum of
-//                                 2^(scale*log2(e)*score), i.e. lse / ln 2
+//   o_part    [B][Hkv][slots][R][D] each partial normalised by its own sum:
+//             fp32 (fp32 inputs), or int16 snorm values o / scale_part
+//             (bf16 inputs; the region is sized for fp32)
+//   scale_part[B][Hkv][slots][R]    fp32, the row's largest |o| (bf16 inputs)
+//   lse_part  [B][Hkv][slots][R]    fp32, log2 of the partial's sum of
+//                                   2^(scale*log2(e)*score), i.e. lse / ln 2
 // Row r of (b, g) is tree node i = r / G of query head g*G + r % G.
 struct PartialArgs {
   const void* q;
@@ -44,7 +47,8 @@ struct PartialArgs {
   const void* kt;
   const void* vt;
   const uint64_t* mask;
-  float* o_part;
+  void* o_part;
+  float* scale_part;
   float* lse_part;
   int B, T, Hq, Hkv, G, R;
   int chunk, max_chunks, slots, max_prefix_len;
@@ -62,7 +66,9 @@ hipError_t launch_partials_mfma(const Plan& plan, PartialArgs args, hipStream_t 
 hipError_t launch_partials_simple(ltree_dtype dtype, const Plan& plan, PartialArgs args,
                                   hipStream_t stream);
 
-hipError_t launch_merge(const Plan& plan, const int32_t* offsets, const float* o_part,
-                        const float* lse_part, float* o, float* lse, hipStream_t stream);
+// snorm: o_part holds int16 snorm values with per-row scales (bf16 path).
+hipError_t launch_merge(const Plan& plan, bool snorm, const int32_t* offsets, const void* o_part,
+                        const float* scale_part, const float* lse_part, float* o, float* lse,
+                        hipStream_t stream);
 
 }  // namespace ltree
