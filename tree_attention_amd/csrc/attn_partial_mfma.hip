@@ -376,52 +376,52 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         }
     }
 
-    // Online softmax in base 2, with a lazily moved reference max.  Each lane
-    // checks its own eight scores against the row threshold; only when some
-    // score would give a probability above 2^8 does the wave reduce the row
-    // maxima across lane groups, move the reference and rescale.  Keeping
-    // probabilities up to 2^8 against a stale reference is exact: the final
-    // normalisation and the lse use the same reference.
-    float lm[NT];
-    bool need = false;
+    // The V^T operands of this block's P.V (rows 16dt + l16, cell 4H + grp),
+    // read now so they arrive during the softmax of the first row tile.
+    f16x8 va[C::DT];
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int uni = S * C::VT + dt * 16 * kVtRow + ((((4 * H) ^ dt) & 4) << 4);
+      va[dt] = *reinterpret_cast<const f16x8*>(sm + voff[dt & 3] + uni);
+    }
+
+    // Online softmax in base 2, with a lazily moved reference max, one row
+    // tile at a time.  Each lane checks its own eight scores against the row
+    // threshold; only when some score would give a probability above 2^8 does
+    // the wave reduce the row maxima across lane groups, move the reference
+    // and rescale.  Keeping probabilities up to 2^8 against a stale reference
+    // is exact: the final normalisation and the lse use the same reference.
+    // The exponentials of tile rt are interleaved with the P.V products of
+    // tile rt-1, so the vector units and the matrix cores work together.
+    f16x8 pprev;
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
       const float m0 = fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), s[0][rt][2]);
       const float m1 = fmaxf(fmaxf(s[0][rt][3], s[1][rt][0]), s[1][rt][1]);
-      lm[rt] = fmaxf(fmaxf(s[1][rt][2], s[1][rt][3]), fmaxf(m0, m1));
-      need = need || lm[rt] > thr[rt];
-    }
-    if (__builtin_expect(__any(need), 0)) {
-      // The scaled accumulator goes back through an MFMA (0*0 + C) so that
-      // every definition of acc inside the loop is an MFMA result and acc
-      // stays in the accumulation registers.
-      const f16x8 z8 = __builtin_bit_cast(f16x8, (u32x4){0u, 0u, 0u, 0u});
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        const float mt = group_max(lm[rt]);
+      const float lm = fmaxf(fmaxf(s[1][rt][2], s[1][rt][3]), fmaxf(m0, m1));
+      if (__builtin_expect(__any(lm > thr[rt]), 0)) {
+        const float mt = group_max(lm);
         const bool up = mt > thr[rt];  // this row's reference moves to mt
-        if (__any(up)) {
-          const float n_new = up ? -mt * c2 : nmc[rt];
-          // nothing accumulated yet (thr = -inf): scale by 0, never by inf
-          const float alpha = !up ? 1.f
-                              : thr[rt] == -INFINITY ? 0.f
-                                                     : __builtin_amdgcn_exp2f(n_new - nmc[rt]);
-          thr[rt] = up ? mt + t8 : thr[rt];
-          nmc[rt] = n_new;
-          lsum[rt] *= alpha;
+        const float n_new = up ? -mt * c2 : nmc[rt];
+        // nothing accumulated yet (thr = -inf): scale by 0, never by inf
+        const float alpha = !up ? 1.f
+                            : thr[rt] == -INFINITY ? 0.f
+                                                   : __builtin_amdgcn_exp2f(n_new - nmc[rt]);
+        thr[rt] = up ? mt + t8 : thr[rt];
+        nmc[rt] = n_new;
+        lsum[rt] *= alpha;
+        // The scaled accumulator goes back through an MFMA (0*0 + C) so that
+        // every definition of acc inside the loop is an MFMA result and acc
+        // stays in the accumulation registers.
+        const f16x8 z8 = __builtin_bit_cast(f16x8, (u32x4){0u, 0u, 0u, 0u});
 #pragma unroll
-          for (int dt = 0; dt < C::DT; ++dt) {
-            acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
-          }
+        for (int dt = 0; dt < C::DT; ++dt) {
+          acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
         }
       }
-    }
 
-    // p = 2^(s*c2 - m*c2) in fp16 for P.V; the row sums add the same fp16
-    // values (dot product with ones, fp32 accumulation)
-    f16x8 pb[NT];
-#pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
+      // p = 2^(s*c2 - m*c2) in fp16 for P.V; the row sums add the same fp16
+      // values (dot product with ones, fp32 accumulation)
       float p[8];
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -435,22 +435,28 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         hp[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
         lsum[rt] = add_f16x2(hp[k], lsum[rt]);
       }
-      pb[rt] = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, hp[0]),
-                                                 __builtin_bit_cast(uint32_t, hp[1]),
-                                                 __builtin_bit_cast(uint32_t, hp[2]),
-                                                 __builtin_bit_cast(uint32_t, hp[3])});
+      const f16x8 pcur = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, hp[0]),
+                                                           __builtin_bit_cast(uint32_t, hp[1]),
+                                                           __builtin_bit_cast(uint32_t, hp[2]),
+                                                           __builtin_bit_cast(uint32_t, hp[3])});
+      // O^T += V^T . P^T for tile rt-1
+      if (rt > 0) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          acc[dt][rt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pprev, acc[dt][rt - 1], 0, 0, 0);
+        }
+        // one MFMA, then three vector instructions, eight times
+#pragma unroll
+        for (int k = 0; k < C::DT; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
+      pprev = pcur;
     }
-
-    // O^T += V^T . P^T; V^T operand of d tile dt: rows 16dt + l16, cell
-    // 4H + grp
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
-      const int uni = S * C::VT + dt * 16 * kVtRow + ((((4 * H) ^ dt) & 4) << 4);
-      const f16x8 va = *reinterpret_cast<const f16x8*>(sm + voff[dt & 3] + uni);
-#pragma unroll
-      for (int rt = 0; rt < NT; ++rt) {
-        acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[rt], acc[dt][rt], 0, 0, 0);
-      }
+      acc[dt][NT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pprev, acc[dt][NT - 1], 0, 0, 0);
     }
   };
 
