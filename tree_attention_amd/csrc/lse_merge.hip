@@ -11,149 +11,161 @@
 //   M = max_s l_s,  w_s = 2^(l_s - M),  Z = sum_s w_s,
 //   o = sum_s (w_s / Z) o_s,  lse = ln 2 * (M + log2 Z).
 //
-// Each output row (b, h, i) is served by NSG groups of D/4 lanes; a lane owns
-// four consecutive features, so every partial row is one coalesced read of 16
-// bytes per lane.  Each group first scans all partial lse values (max, then
-// sum), then accumulates its share of the partial outputs (splits q, q+NSG,
-// ...) in a fixed order; the groups' sums are added in LDS in a fixed order,
-// so the result is bitwise deterministic.  Splitting the partials over groups
-// keeps several times more loads in flight than one group per row would.
+// One wavefront per output row (b, h, i).  Lane s first loads the lse (and,
+// on the bf16 path, the scale) of partial s, 64 partials at a time; the
+// wavefront reduces max and sum across lanes and forms each partial's weight
+// in its lane.  Then every lane owns D/64 consecutive features: per partial it
+// reads them (one coalesced row read per partial, several partials in flight)
+// and adds them with the partial's weight, read from lane s as a scalar.  The
+// order of additions is fixed, so the result is bitwise deterministic.
 #include "ltree_internal.h"
 
 namespace ltree {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+constexpr int kMergeWaves = 4;  // rows per workgroup
+constexpr int kBatch = 64;      // partials per pass (one per lane)
+constexpr int kUnroll = 8;      // partial rows in flight per lane
 
-template <int LPR>
-__device__ inline float group_max(float v) {
+__device__ inline float wave_max(float v) {
 #pragma unroll
-  for (int s = LPR / 2; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
+  return v;
+}
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
   return v;
 }
 
-template <int LPR>
-__device__ inline float group_sum(float v) {
-#pragma unroll
-  for (int s = LPR / 2; s >= 1; s >>= 1) v += __shfl_xor(v, s);
-  return v;
+// lane s's value as a wavefront-uniform scalar
+__device__ inline float lane_value(float v, int s) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), s));
 }
 
-constexpr int kMergeThreads = 256;
-constexpr int kSplitGroups = 4;  // lane groups sharing one output row
-
-// Four features of partial row pr for lane j: fp32, or int16 snorm values
-// times the row's scale.
+// The D/64 features of partial row pr owned by lane j: fp32, or int16 snorm
+// values (the row's scale is applied through the weight).
 template <int D, bool SNORM>
-__device__ inline f32x4 load_part(const void* o_part, const float* scale_part, size_t pr, int j) {
+__device__ inline void load_part(const void* o_part, size_t pr, int j, float (&v)[D / 64]) {
+  constexpr int FPL = D / 64;
   if constexpr (SNORM) {
-    const s16x4 q = reinterpret_cast<const s16x4*>(static_cast<const int16_t*>(o_part) + pr * D)[j];
-    const float sc = scale_part[pr] * (1.f / 32767.f);
-    return (f32x4){static_cast<float>(q[0]), static_cast<float>(q[1]), static_cast<float>(q[2]),
-                   static_cast<float>(q[3])} * sc;
+    const int16_t* p = static_cast<const int16_t*>(o_part) + pr * D + j * FPL;
+    if constexpr (FPL == 2) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(p);
+      v[0] = static_cast<float>(static_cast<int16_t>(u & 0xffffu));
+      v[1] = static_cast<float>(static_cast<int16_t>(u >> 16));
+    } else {
+      v[0] = static_cast<float>(*p);
+    }
   } else {
-    return reinterpret_cast<const f32x4*>(static_cast<const float*>(o_part) + pr * D)[j];
+    const float* p = static_cast<const float*>(o_part) + pr * D + j * FPL;
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) v[f] = p[f];
   }
 }
 
 template <int D, bool SNORM>
-__global__ __launch_bounds__(kMergeThreads) void lse_merge_kernel(
+__global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     const int32_t* __restrict__ offsets, const void* __restrict__ o_part,
     const float* __restrict__ scale_part, const float* __restrict__ lse_part,
     float* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv, int G, int R,
     int chunk, int slots, int max_prefix_len) {
-  constexpr int LPR = D / 4;                             // lanes per group
-  constexpr int NSG = kSplitGroups;
-  constexpr int RPB = kMergeThreads / (LPR * NSG);       // rows per workgroup
-  __shared__ f32x4 red[NSG - 1][RPB][LPR];
-
-  const int j = threadIdx.x % LPR;                       // lane within the group
-  const int q = (threadIdx.x / LPR) % NSG;               // split group
-  const int rl = threadIdx.x / (LPR * NSG);              // row within the workgroup
+  constexpr int FPL = D / 64;  // features per lane
+  const int j = threadIdx.x & 63;
   // rows are ordered (b, h, i) so the lse writes [B, Hq, T] are contiguous;
   // B * Hq * T < 2^31 is checked by the host
-  const unsigned row = blockIdx.x * RPB + rl;
-  const unsigned nrows = static_cast<unsigned>(B) * Hq * T;
-  const bool valid = row < nrows;
-  const unsigned i = valid ? row % T : 0;
-  const unsigned bh = valid ? row / T : 0;
+  const unsigned row = blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+  if (row >= static_cast<unsigned>(B) * Hq * T) return;  // whole wavefronts
+  const unsigned i = row % T;
+  const unsigned bh = row / T;
   const unsigned h = bh % Hq;
   const unsigned b = bh / Hq;
   const unsigned g = h / G;
   const unsigned r = i * G + (h % G);
+  float* orow = o + ((static_cast<size_t>(b) * T + i) * Hq + h) * D + j * FPL;
+  float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * T + i;
 
   const int L = offsets[b + 1] - offsets[b];
-  const bool bad = L < 0 || L > max_prefix_len;
-  // one partial per prefix split, the last of which also covers the tree
-  // keys; one tree-only partial when the prefix is empty
-  const int nparts = bad || L == 0 ? 1 : (L + chunk - 1) / chunk;
-  const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
-  auto part_row = [&](int s) { return (base + s) * R + r; };
-
-  float mx = -INFINITY;
-  for (int s = j; s < nparts; s += LPR) mx = fmaxf(mx, lse_part[part_row(s)]);
-  mx = group_max<LPR>(mx);
-  float z = 0.f;
-  for (int s = j; s < nparts; s += LPR) z += exp2f(lse_part[part_row(s)] - mx);
-  z = group_sum<LPR>(z);
-  const float inv_z = 1.f / z;
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  constexpr int U = 4;  // partials in flight per lane and step
-  int s = q;
-  for (; s + (U - 1) * NSG < nparts; s += U * NSG) {
-    float w[U];
-    f32x4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const size_t pr = part_row(s + u * NSG);
-      w[u] = lse_part[pr];
-      v[u] = load_part<D, SNORM>(o_part, scale_part, pr, j);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) acc += (exp2f(w[u] - mx) * inv_z) * v[u];
-  }
-  for (; s < nparts; s += NSG) {
-    const size_t pr = part_row(s);
-    acc += (exp2f(lse_part[pr] - mx) * inv_z) * load_part<D, SNORM>(o_part, scale_part, pr, j);
-  }
-
-  if (q > 0) red[q - 1][rl][j] = acc;
-  __syncthreads();
-  if (q > 0 || !valid) return;
-#pragma unroll
-  for (int k = 0; k < NSG - 1; ++k) acc += red[k][rl][j];
-  f32x4* orow = reinterpret_cast<f32x4*>(o + ((static_cast<size_t>(b) * T + i) * Hq + h) * D) + j;
-  float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * T + i;
-  if (bad) {
+  if (L < 0 || L > max_prefix_len) {
     // The prefix-length table disagrees with max_prefix_len: fail loudly.
     const float nan = __builtin_nanf("");
-    *orow = (f32x4){nan, nan, nan, nan};
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) orow[f] = nan;
     if (j == 0) *lrow = nan;
     return;
   }
-  *orow = acc;
+  // one partial per prefix split, the last of which also covers the tree
+  // keys; one tree-only partial when the prefix is empty
+  const int nparts = L == 0 ? 1 : (L + chunk - 1) / chunk;
+  const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
+  auto part_row = [&](int s) { return (base + s) * R + r; };
+
+  // max and sum of 2^lse over all partials
+  float mx = -INFINITY;
+  for (int s0 = 0; s0 < nparts; s0 += kBatch) {
+    if (s0 + j < nparts) mx = fmaxf(mx, lse_part[part_row(s0 + j)]);
+  }
+  mx = wave_max(mx);
+  float z = 0.f;
+  for (int s0 = 0; s0 < nparts; s0 += kBatch) {
+    if (s0 + j < nparts) z += exp2f(lse_part[part_row(s0 + j)] - mx);
+  }
+  z = wave_sum(z);
+  const float inv_z = 1.f / z;
+
+  float acc[FPL];
+#pragma unroll
+  for (int f = 0; f < FPL; ++f) acc[f] = 0.f;
+  for (int s0 = 0; s0 < nparts; s0 += kBatch) {
+    const int n = min(kBatch, nparts - s0);
+    // this lane's weight: partial s0 + j
+    float wl = 0.f;
+    if (j < n) {
+      const size_t pr = part_row(s0 + j);
+      wl = exp2f(lse_part[pr] - mx) * inv_z;
+      if constexpr (SNORM) wl *= scale_part[pr] * (1.f / 32767.f);
+    }
+    int s = 0;
+    for (; s + kUnroll <= n; s += kUnroll) {
+      float v[kUnroll][FPL];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) load_part<D, SNORM>(o_part, part_row(s0 + s + u), j, v[u]);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const float w = lane_value(wl, s + u);
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) acc[f] = fmaf(w, v[u][f], acc[f]);
+      }
+    }
+    for (; s < n; ++s) {
+      float v[FPL];
+      load_part<D, SNORM>(o_part, part_row(s0 + s), j, v);
+      const float w = lane_value(wl, s);
+#pragma unroll
+      for (int f = 0; f < FPL; ++f) acc[f] = fmaf(w, v[f], acc[f]);
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < FPL; ++f) orow[f] = acc[f];
   if (j == 0) *lrow = (mx + log2f(z)) * 0.6931471805599453f;
 }
-
-}  // namespace
 
 template <int D, bool SNORM>
 void launch_typed(const Plan& p, dim3 grid, const int32_t* offsets, const void* o_part,
                   const float* scale_part, const float* lse_part, float* o, float* lse,
                   hipStream_t stream) {
-  hipLaunchKernelGGL((lse_merge_kernel<D, SNORM>), grid, dim3(kMergeThreads), 0, stream, offsets,
-                     o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G, p.R,
-                     p.chunk, p.slots, p.max_prefix_len);
+  hipLaunchKernelGGL((lse_merge_kernel<D, SNORM>), grid, dim3(64 * kMergeWaves), 0, stream,
+                     offsets, o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G,
+                     p.R, p.chunk, p.slots, p.max_prefix_len);
 }
+
+}  // namespace
 
 hipError_t launch_merge(const Plan& p, bool snorm, const int32_t* offsets, const void* o_part,
                         const float* scale_part, const float* lse_part, float* o, float* lse,
                         hipStream_t stream) {
   const long rows = static_cast<long>(p.B) * p.Hq * p.T;
-  const long rows_per_block = kMergeThreads / (p.D / 4 * kSplitGroups);
-  const dim3 grid(static_cast<unsigned>((rows + rows_per_block - 1) / rows_per_block));
+  const dim3 grid(static_cast<unsigned>((rows + kMergeWaves - 1) / kMergeWaves));
   if (p.D == 128) {
     if (snorm) {
       launch_typed<128, true>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
