@@ -9,7 +9,9 @@ several copies of the prefix KV cache, together larger than the 256 MB
 Infinity Cache, so every step streams its keys from HBM (cold-cache timing).
 
 Prints one JSON line.  The throughput `value` is algorithmic TFLOP/s of the
-whole call (wall clock over the timed steps); `roofline` rates the dominant
+whole call (wall clock over the timed steps, launched as one HIP graph;
+`us_per_call_eager` gives the same steps launched call by call); `roofline`
+rates the dominant
 kernel (the partial-attention kernel) against the bf16 MFMA peak, with its
 duration taken from HIP events recorded on the launch stream around K
 back-to-back launches of it on the same rotating inputs.
@@ -205,17 +207,30 @@ def main():
         assert step(s) == 0
     torch.cuda.synchronize()
 
-    # the timed region: K whole steps back to back
+    # the timed region: K whole steps back to back, launched as one HIP graph
+    # (a serving loop replays the same launches every verification step), and
+    # the same K steps launched one call at a time for comparison
     K = args.steps
-    log(f"timing {K} steps")
+    log(f"capturing {K} steps in a graph")
+    steps_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(steps_graph):
+        for s in range(K):
+            step(s)
+    steps_graph.replay()
     torch.cuda.synchronize()
+    log(f"timing {K} steps")
+    t0 = time.perf_counter()
+    steps_graph.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1000 / K
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
     t0 = time.perf_counter()
     for s in range(K):
         step(s)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1000 / K
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    ms_per_step_eager = (t1 - t0) * 1000 / K
 
     # the dominant kernel alone: K launches back to back between two events on
     # the launch stream (events around every launch would add a cache flush
@@ -256,6 +271,7 @@ def main():
             "cache": "hot (one KV copy)" if args.hot else f"cold ({n_copies} rotating KV copies)",
         },
         "us_per_call": round(us, 2),
+        "us_per_call_eager": round(ms_per_step_eager * 1000, 2),
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "hbm_frac": round(bytes_alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "mask_build_us": round(mask_us, 2),

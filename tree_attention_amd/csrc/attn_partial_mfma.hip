@@ -37,17 +37,25 @@
 // 8g..8g+7 of the block, exactly the k-slots the P.V MFMA expects from lane
 // group g, so probabilities never move between lanes.
 //
+// Order within a block: the K operands of the block are already in
+// registers (loaded during the previous P.V); the QK products run one row
+// tile at a time, each row tile's softmax overlapping the products of the
+// next; then the P.V products, one d tile at a time, while the K operands of
+// the following block are read.
+//
 // LDS.  Three stages of one tile each hold K [64 keys][D] and the raw V tile,
-// both filled straight from memory by global_load_lds (16 bytes per lane), so
-// no staging registers are needed and two tiles can be in flight while one is
-// computed.  Once a thread's V loads of the next tile have landed it converts
-// them to fp16 and writes them transposed into one of two V^T buffers
-// [D][64 keys] (exact for |v| < 65504).  Probabilities enter the P.V product
-// as fp16, whose rounding (2^-11) keeps the output within tolerance even where
-// a few large values dominate a row, which bf16 (2^-8) does not.  LDS has 64
-// banks of 4 bytes (16 lanes per cycle for 16-byte accesses, 64 for 4-byte
-// ones); the K chunk swizzle and the V^T row pitch and cell swizzle make every
-// operand read and every V^T write conflict-free.  One barrier per tile.
+// both filled straight from memory by buffer loads to LDS (16 bytes per lane;
+// the buffer range ends at the tile's last real key, so rows past it read as
+// zeros), so no staging registers are needed and tiles t+1 and t+2 are in
+// flight while tile t is computed.  Once a thread's V loads of the next tile
+// have landed it converts them to fp16 and writes them transposed into one of
+// three V^T buffers [D][64 keys] (exact for |v| < 65504).  Probabilities
+// enter the P.V product as fp16, whose rounding (2^-11) keeps the output
+// within tolerance even where a few large values dominate a row, which bf16
+// (2^-8) does not.  LDS has 64 banks of 4 bytes (16 lanes per cycle for
+// 16-byte accesses, 64 for 4-byte ones); the K chunk swizzle and the V^T row
+// pitch and cell swizzle make every operand read and every V^T write
+// conflict-free.  One barrier per tile.
 #include <type_traits>
 
 #include "ltree_internal.h"
@@ -69,6 +77,8 @@ constexpr int kWaves = 8;    // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgroup)
 constexpr int kVtRow = 144;  // bytes per V^T row: 64 fp16 keys + 16 bytes of pitch
+// fourth word of a raw buffer descriptor (32-bit data format; no swizzle)
+constexpr int kBufferFlags = 0x00020000;
 
 template <int D>
 struct Cfg {
@@ -86,9 +96,10 @@ struct Cfg {
   static constexpr int KDMA = kTile * KC16 / kThreads;    // K 16-byte DMA loads per thread
   static constexpr int ROWS_PER_DMA = 1024 / ROW;         // K rows per wave DMA instruction
   static constexpr int VITEMS = (kTile / 2) * KC16;       // V items: (key pair, d chunk)
-  static constexpr int VWAVES = VITEMS / 64;              // waves that stage V
-  static constexpr int DPT_V = KDMA + 2;                  // DMA per tile, V-staging waves
-  static constexpr int DPT_K = KDMA;                      // DMA per tile, other waves
+  static constexpr int VIPT = VITEMS > kThreads ? VITEMS / kThreads : 1;  // V items per thread
+  static constexpr int VTHREADS = VITEMS / VIPT;          // threads that stage V
+  static constexpr int DPT_V = KDMA + 2 * VIPT;           // DMA per tile, V-staging threads
+  static constexpr int DPT_K = KDMA;                      // DMA per tile, other threads
 };
 
 // K rows: the 16 lanes of one lane group read keys 8a + b (+4), a, b in 0..3,
@@ -133,21 +144,18 @@ __device__ inline float group_sum(float x) {
 // else to memory).
 template <int DPT>
 __device__ inline void wait_dma_except(int n) {
-  static_assert(DPT >= 1 && DPT <= 4, "vmcnt table");
   if (n >= 1) {
-    if constexpr (DPT == 4) {
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else if constexpr (DPT == 3) {
-      asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-    } else if constexpr (DPT == 2) {
-      asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-    }
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DPT) : "memory");
   } else {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
 }
+
+// Workgroup barrier for the hand-off of LDS buffers: this wave's LDS reads
+// and writes are complete; its tile loads in flight are not waited for
+// (__syncthreads would wait for them all: each thread waits for its own
+// loads of a tile before the barrier that publishes it).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // acc + lo + hi of two fp16 (the row sums)
 __device__ inline float add_f16x2(f16x2 h, float acc) {
@@ -215,25 +223,39 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     }
   }
 
-  // Online softmax state per row, in raw score units s = q.k, relative to a
-  // reference max m of the row:
-  //   thr   m + 8/c2: a score above it would give a probability above 2^8
-  //         (-inf while the row has seen no key),
-  //   nmc   -m*c2, the exponent offset (0 while the row has seen no key),
-  //   lsum  sum of this lane's probabilities as rounded to fp16 for P.V (the
-  //         output is normalised by the same values it accumulates).
-  f32x4 acc[C::DT][NT];
-  float thr[NT], nmc[NT], lsum[NT];
+  // Wait for these loads here, before any tile load is in flight (a later
+  // first use would make the wait cover the tile loads too).
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
-    thr[rt] = -INFINITY;
-    nmc[rt] = 0.f;
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c) asm volatile("" : "+v"(qf[rt][c]));
+    asm volatile("" : "+v"(vbits[rt]));
+  }
+
+  // Online softmax state per row, in raw score units s = q.k, relative to a
+  // reference max m of the row:
+  //   nmc   -m*c2, the exponent offset (kNoRef while the row has seen no
+  //         key: far above any real offset, so the first key moves the
+  //         reference and scales the empty accumulator by 2^-kNoRef = 0,
+  //         and masked scores still give 2^-inf = 0, never inf - inf),
+  //   thr   m + 8/c2 = -nmc/c2 + 8/c2, formed when needed: a score above it
+  //         would give a probability above 2^8,
+  //   lsum  sum of this lane's probabilities as rounded to fp16 for P.V (the
+  //         output is normalised by the same values it accumulates).
+  constexpr float kNoRef = 1e30f;
+  f32x4 acc[C::DT][NT];
+  float nmc[NT], lsum[NT];
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    nmc[rt] = kNoRef;
     lsum[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;
-  const float t8 = 8.f / c2;
+  const float t8 = a.headroom;             // 8 / c2
+  const float nic2 = a.neg_inv_scale_log2;  // -1 / c2
+  auto thr = [&](int rt) { return fmaf(nmc[rt], nic2, t8); };
   // prefix tiles, then one tree tile (T <= 64)
   const int ptiles = (npk + kTile - 1) / kTile;
   const int ntiles = ptiles + (tree ? 1 : 0);
@@ -265,65 +287,79 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // every stage index below is a compile-time constant (the tile loop is
   // unrolled by three).
   // K: 16-byte chunks straight to the K tile, swizzled by key.
-  // V: item (key pair m, d chunk c) of thread tid < VITEMS: keys 2m and 2m+1
-  // of chunk c land in two 1 KB slots of the raw V tile at this lane's
-  // position, so only this thread reads them back.
+  // V: item (key pair m, d chunk c), VIPT per thread: item tid + i * kThreads
+  // (threads below VTHREADS); keys 2m and 2m+1 of chunk c land in two 1 KB
+  // slots of the raw V tile at this lane's position, so only this thread
+  // reads them back.
   char* const sm = x.smem;
-  const bool vstage = wave < C::VWAVES;
-  const int vm = tid / C::KC16, vc = tid % C::KC16;
-  // per-thread source offsets (elements) within a tile; a prefix tile further
-  // is 64 * kstride elements on
+  const bool vstage = tid < C::VTHREADS;
+  // Loads go through buffer descriptors whose range ends with the tile's last
+  // real key, so rows past it read as zeros (and are masked); per-thread byte
+  // offsets within a tile:
   int ksoff[C::KDMA];
-  int krow[C::KDMA];
 #pragma unroll
   for (int j = 0; j < C::KDMA; ++j) {
-    const int blk = j * kWaves + wave;
-    krow[j] = blk * C::ROWS_PER_DMA + lane / C::KC16;
-    const int slotc = lane % C::KC16;
-    ksoff[j] = krow[j] * kstride + ((slotc ^ kswz<D>(krow[j])) * 8);
+    const int row = (j * kWaves + wave) * C::ROWS_PER_DMA + lane / C::KC16;
+    ksoff[j] = (row * kstride + (((lane % C::KC16) ^ kswz<D>(row)) * 8)) * 2;
   }
-  const int vsoff = (2 * vm) * kstride + vc * 8;
-  const long tstep = static_cast<long>(kTile) * kstride;
-  auto dma = [&](auto S_, int t) {
-    constexpr int S = decltype(S_)::value;
-    // rows past the end of the keys repeat the last key (masked later)
+  int vsoff[C::VIPT][2];
+#pragma unroll
+  for (int i = 0; i < C::VIPT; ++i) {
+    const int it = tid + i * kThreads, vm = it / C::KC16, vc = it % C::KC16;
+    vsoff[i][0] = ((2 * vm) * kstride + vc * 8) * 2;
+    vsoff[i][1] = vsoff[i][0] + kstride * 2;
+  }
+  auto dma = [&](int S, int t) {
     const bool tt = t == ptiles;  // the tree tile
-    const bool full = !tt && (t + 1) * kTile <= npk;
-    const int last = tt ? T - 1 : npk - 1 - t * kTile;
-    const __bf16* kb = tt ? x.ktree : x.kbase + t * tstep;
-    const __bf16* vb = tt ? x.vtree : x.vbase + t * tstep;
+    const int nrows = tt ? T : min(kTile, npk - t * kTile);
+    const size_t toff = tt ? 0 : static_cast<size_t>(t) * kTile * kstride;
+    const int bytes = nrows * kstride * 2;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>((tt ? x.ktree : x.kbase) + toff), 0, bytes, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<__bf16*>((tt ? x.vtree : x.vbase) + toff), 0, bytes, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < C::KDMA; ++j) {
-      const __bf16* src = full ? kb + ksoff[j] : kb + ksoff[j] + (min(krow[j], last) - krow[j]) * kstride;
       char* dst = sm + Cfg<D>::K0 + S * Cfg<D>::BUF + (j * kWaves + wave) * 1024;
-      __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+      const int vo = ksoff[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)dst, 16, vo, 0, 0, 0);
     }
     if (vstage) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const __bf16* src = full ? vb + vsoff + j * kstride
-                                 : vb + vsoff + (min(2 * vm + j, last) - 2 * vm) * kstride;
-        char* dst = sm + Cfg<D>::R0 + S * Cfg<D>::BUF + (j * Cfg<D>::VWAVES + wave) * 1024;
-        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
-      }
+      for (int i = 0; i < C::VIPT; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          char* dst = sm + Cfg<D>::R0 + S * Cfg<D>::BUF +
+                      (j * (Cfg<D>::VITEMS / 64) + i * kWaves + wave) * 1024;
+          const int vo = vsoff[i][j];
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)dst, 16, vo, 0, 0, 0);
+        }
     }
   };
-  // This thread's V item, bf16 -> fp16, transposed into V^T buffer S: for
+  // This thread's V items, bf16 -> fp16, transposed into V^T buffer S: for
   // each feature d = 8c + e, the dword (key 2m, key 2m+1); the eight cells of
-  // a thread are 144 bytes apart (vt_off is linear in e for d = 8c + e).
+  // an item are 144 bytes apart (vt_off is linear in e for d = 8c + e).
   int rdoff = C::R0 + wave * 1024 + 16 * lane;
-  int wroff = C::T0 + vt_off(8 * vc, vm >> 2) + 4 * (vm & 3);
-  asm volatile("" : "+v"(rdoff), "+v"(wroff));
-  auto convert = [&](auto S_) {
-    constexpr int S = decltype(S_)::value;
-    if (vstage) {
-      const char* rb = sm + rdoff + S * C::BUF;
-      const u32x4 u0 = *reinterpret_cast<const u32x4*>(rb);
-      const u32x4 u1 = *reinterpret_cast<const u32x4*>(rb + C::VWAVES * 1024);
-      char* wb = sm + wroff + S * C::VT;
+  int wroff[C::VIPT];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        *reinterpret_cast<uint32_t*>(wb + e * kVtRow) = pack_f16_of_bf16(u0[e >> 1], u1[e >> 1], e & 1);
+  for (int i = 0; i < C::VIPT; ++i) {
+    const int it = tid + i * kThreads, vm = it / C::KC16, vc = it % C::KC16;
+    wroff[i] = C::T0 + vt_off(8 * vc, vm >> 2) + 4 * (vm & 3);
+    asm volatile("" : "+v"(wroff[i]));
+  }
+  asm volatile("" : "+v"(rdoff));
+  auto convert = [&](int S) {
+    if (vstage) {
+#pragma unroll
+      for (int i = 0; i < C::VIPT; ++i) {
+        const char* rb = sm + rdoff + S * C::BUF + i * kWaves * 1024;
+        const u32x4 u0 = *reinterpret_cast<const u32x4*>(rb);
+        const u32x4 u1 = *reinterpret_cast<const u32x4*>(rb + (C::VITEMS / 64) * 1024);
+        char* wb = sm + wroff[i] + S * C::VT;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          *reinterpret_cast<uint32_t*>(wb + e * kVtRow) = pack_f16_of_bf16(u0[e >> 1], u1[e >> 1], e & 1);
+        }
       }
     }
   };
@@ -337,162 +373,209 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
 
   // ---- one 32-key block: block half H of the tile in stage S, whose first
   // `valid` keys are real (prefix or tree keys); tree blocks also apply the
-  // ancestor mask
-  auto block = [&](auto S_, auto H_, int valid, bool treeblk) {
-    constexpr int S = decltype(S_)::value;
+  // ancestor mask.
+  //
+  // The K operands of a block (all d chunks, both 16-key halves) are loaded
+  // into registers ahead of it, during the P.V of the block before, so its
+  // QK products start at once.  The QK products run one row tile at a time,
+  // and the softmax of row tile rt is computed while the products of row tile
+  // rt+1 are in the matrix cores.  The P.V products follow once every row
+  // tile has its probabilities, one d tile of V^T at a time.
+  bf16x8 ka[C::DC][2];
+  auto kload = [&](int S, auto H_) {
     constexpr int H = decltype(H_)::value;
-    // S^T = K . Q^T
-    f32x4 s[2][NT];
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c) {
-      bf16x8 ka[2];
+    for (int c = 0; c < C::DC; ++c)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        ka[sub] = *reinterpret_cast<const bf16x8*>(sm + koff[c] + S * C::BUF + H * 32 * C::ROW +
-                                                   sub * 4 * C::ROW);
-      }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int rt = 0; rt < NT; ++rt) {
-          s[sub][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              ka[sub], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub][rt], 0, 0, 0);
-        }
-      }
-    }
+      for (int sub = 0; sub < 2; ++sub)
+        ka[c][sub] = *reinterpret_cast<const bf16x8*>(sm + koff[c] + S * C::BUF + H * 32 * C::ROW +
+                                                      sub * 4 * C::ROW);
+  };
+  f16x8 P[NT];  // probabilities of the current block (the B operand P^T of P.V)
 
-    // keys past the end, and tree keys outside the row's branch
-    if (treeblk || valid < 32) {
+  // S^T = K . Q^T for row tile rt; keys past the end, and tree keys outside
+  // the row's branch, get -inf
+  auto qk = [&](f32x4 (&s)[2], int rt, int H, int valid, bool treeblk, auto MASK_) {
+#pragma unroll
+    for (int c = 0; c < C::DC; ++c)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            ka[c][sub], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub], 0, 0, 0);
+    if constexpr (decltype(MASK_)::value) {
+      // one bit per key of this lane: real key and (tree) an ancestor; made
+      // opaque so the per-key conditions are formed here, not kept for the
+      // whole loop
+      const int nin = min(max(valid - 8 * grp, 0), 8);
+      uint32_t bits = (!treeblk ? 0xffu : H ? (vbits[rt] >> 8) : vbits[rt]) & ((1u << nin) - 1u);
+      asm volatile("" : "+v"(bits));
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const bool in = 8 * grp + 4 * sub + v < valid;
-#pragma unroll
-          for (int rt = 0; rt < NT; ++rt) {
-            const uint32_t bits = !treeblk ? 0xffu : H ? (vbits[rt] >> 8) : vbits[rt];
-            if (!(in && ((bits >> (4 * sub + v)) & 1u))) s[sub][rt][v] = -INFINITY;
-          }
+          if (!((bits >> (4 * sub + v)) & 1u)) s[sub][v] = -INFINITY;
         }
     }
+  };
+  // p = 2^(s*c2 - m*c2) in fp16 for P.V, and their sum (the same fp16
+  // values, accumulated in fp32)
+  auto probs = [&](const f32x4 (&s)[2], int rt, float& bsum) {
+    float p[8];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) p[4 * sub + v] = __builtin_amdgcn_exp2f(fmaf(s[sub][v], c2, nmc[rt]));
+    f16x2 hp[4];
+    bsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      hp[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
+      bsum = add_f16x2(hp[k], bsum);
+    }
+    P[rt] = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, hp[0]),
+                                              __builtin_bit_cast(uint32_t, hp[1]),
+                                              __builtin_bit_cast(uint32_t, hp[2]),
+                                              __builtin_bit_cast(uint32_t, hp[3])});
+  };
+  auto lane_max = [](const f32x4 (&s)[2]) {
+    const float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    const float m1 = fmaxf(fmaxf(s[0][3], s[1][0]), s[1][1]);
+    return fmaxf(fmaxf(s[1][2], s[1][3]), fmaxf(m0, m1));
+  };
 
-    // The V^T operands of this block's P.V (rows 16dt + l16, cell 4H + grp),
-    // read now so they arrive during the softmax of the first row tile.
+  // Move row tile rt's references to the block's row maxima where a score
+  // passed the threshold, and rescale what it has accumulated.
+  auto rescale = [&](int rt, float lm) {
+    const float mt = group_max(lm);
+    const bool up = mt > thr(rt);  // this row's reference moves to mt
+    const float n_new = up ? -mt * c2 : nmc[rt];
+    const float alpha = up ? __builtin_amdgcn_exp2f(n_new - nmc[rt]) : 1.f;
+    nmc[rt] = n_new;
+    lsum[rt] *= alpha;
+    // The scaled accumulator goes back through an MFMA (0*0 + C) so that
+    // every definition of acc inside the loop is an MFMA result and acc
+    // stays in the accumulation registers.
+    const f16x8 z8 = __builtin_bit_cast(f16x8, (u32x4){0u, 0u, 0u, 0u});
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
+    }
+  };
+
+  // Online softmax in base 2, with a lazily moved reference max.  Each lane
+  // checks its own eight scores of a row against the row threshold; only
+  // when some score would give a probability above 2^8 does the wave reduce
+  // the row maxima across lane groups, move the reference and rescale.
+  // Keeping probabilities up to 2^8 against a stale reference is exact: the
+  // final normalisation and the lse use the same reference.
+  //
+  // Row tile by row tile: the check of row tile rt, then its exponentials
+  // with the QK products of row tile rt+1 in flight.
+  auto qk_softmax = [&](auto H_, int valid, bool treeblk, auto MASK_) {
+    constexpr int H = decltype(H_)::value;
+    f32x4 s[2][2];
+    float lm[2];
+    qk(s[0], 0, H, valid, treeblk, MASK_);
+    lm[0] = lane_max(s[0]);
+#pragma unroll
+    for (int rt = 0; rt < NT; ++rt) {
+      if (__builtin_expect(__any(lm[rt & 1] > thr(rt)), 0)) rescale(rt, lm[rt & 1]);
+      float bsum;
+      probs(s[rt & 1], rt, bsum);
+      lsum[rt] += bsum;
+      if (rt + 1 < NT) {
+        qk(s[(rt + 1) & 1], rt + 1, H, valid, treeblk, MASK_);
+        lm[(rt + 1) & 1] = lane_max(s[(rt + 1) & 1]);
+        // issue order: the products of row tile rt+1 one at a time between
+        // the vector instructions of row tile rt
+#pragma unroll
+        for (int k = 0; k < 2 * C::DC; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+        }
+      }
+    }
+  };
+
+  // O^T += V^T . P^T for block half H of stage S, one d tile at a time;
+  // `next` loads the K operands of the following block meanwhile
+  auto pv = [&](int S, auto H_, auto next) {
+    constexpr int H = decltype(H_)::value;
+    // V^T rows 16dt + l16, cell 4H + grp
     f16x8 va[C::DT];
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
       const int uni = S * C::VT + dt * 16 * kVtRow + ((((4 * H) ^ dt) & 4) << 4);
       va[dt] = *reinterpret_cast<const f16x8*>(sm + voff[dt & 3] + uni);
     }
-
-    // Online softmax in base 2, with a lazily moved reference max, one row
-    // tile at a time.  Each lane checks its own eight scores against the row
-    // threshold; only when some score would give a probability above 2^8 does
-    // the wave reduce the row maxima across lane groups, move the reference
-    // and rescale.  Keeping probabilities up to 2^8 against a stale reference
-    // is exact: the final normalisation and the lse use the same reference.
-    // The exponentials of tile rt are interleaved with the P.V products of
-    // tile rt-1, so the vector units and the matrix cores work together.
-    f16x8 pprev;
+    next();
 #pragma unroll
-    for (int rt = 0; rt < NT; ++rt) {
-      const float m0 = fmaxf(fmaxf(s[0][rt][0], s[0][rt][1]), s[0][rt][2]);
-      const float m1 = fmaxf(fmaxf(s[0][rt][3], s[1][rt][0]), s[1][rt][1]);
-      const float lm = fmaxf(fmaxf(s[1][rt][2], s[1][rt][3]), fmaxf(m0, m1));
-      if (__builtin_expect(__any(lm > thr[rt]), 0)) {
-        const float mt = group_max(lm);
-        const bool up = mt > thr[rt];  // this row's reference moves to mt
-        const float n_new = up ? -mt * c2 : nmc[rt];
-        // nothing accumulated yet (thr = -inf): scale by 0, never by inf
-        const float alpha = !up ? 1.f
-                            : thr[rt] == -INFINITY ? 0.f
-                                                   : __builtin_amdgcn_exp2f(n_new - nmc[rt]);
-        thr[rt] = up ? mt + t8 : thr[rt];
-        nmc[rt] = n_new;
-        lsum[rt] *= alpha;
-        // The scaled accumulator goes back through an MFMA (0*0 + C) so that
-        // every definition of acc inside the loop is an MFMA result and acc
-        // stays in the accumulation registers.
-        const f16x8 z8 = __builtin_bit_cast(f16x8, (u32x4){0u, 0u, 0u, 0u});
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
-        }
-      }
-
-      // p = 2^(s*c2 - m*c2) in fp16 for P.V; the row sums add the same fp16
-      // values (dot product with ones, fp32 accumulation)
-      float p[8];
+      for (int rt = 0; rt < NT; ++rt)
+        acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], P[rt], acc[dt][rt], 0, 0, 0);
+    // issue order: two V^T reads ahead, then per d tile its products and one
+    // more read (the last two d tiles: the next block's K operands, DC each)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          p[4 * sub + v] = __builtin_amdgcn_exp2f(fmaf(s[sub][rt][v], c2, nmc[rt]));
-        }
-      f16x2 hp[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        hp[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
-        lsum[rt] = add_f16x2(hp[k], lsum[rt]);
-      }
-      const f16x8 pcur = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, hp[0]),
-                                                           __builtin_bit_cast(uint32_t, hp[1]),
-                                                           __builtin_bit_cast(uint32_t, hp[2]),
-                                                           __builtin_bit_cast(uint32_t, hp[3])});
-      // O^T += V^T . P^T for tile rt-1
-      if (rt > 0) {
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt) {
-          acc[dt][rt - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pprev, acc[dt][rt - 1], 0, 0, 0);
-        }
-        // one MFMA, then three vector instructions, eight times
-#pragma unroll
-        for (int k = 0; k < C::DT; ++k) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        }
-      }
-      pprev = pcur;
+    for (int dt = 0; dt + 2 < C::DT; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      acc[dt][NT - 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], pprev, acc[dt][NT - 1], 0, 0, 0);
+    for (int dt = 0; dt < 2; ++dt) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, Cfg<D>::DC, 0);
     }
   };
 
-  // ---- Schedule.  Per tile t: barrier (V^T of
-  // tile t written by every thread; the buffers of tile t-1 free), load tile
-  // t+2 into them, compute tile t, then wait for this thread's loads of tile
-  // t+1 and convert them.
+  // ---- Schedule.  One barrier per tile, before the P.V of its last block:
+  // by then every thread has converted its V items of tile t+1 (so V^T of
+  // tile t+1 and, through the loads it waited for, K of tile t+1 are
+  // complete), and every wave has finished reading K of tile t (whose stage
+  // then takes the loads of tile t+3) and the V^T of tile t-1.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  auto tile = [&](auto S_, int t) {
-    constexpr int S = decltype(S_)::value;
-    using SN = std::integral_constant<int, (S + 1) % kStages>;
-    using SNN = std::integral_constant<int, (S + 2) % kStages>;
-    __syncthreads();
-    if (t + 2 < ntiles) dma(SNN{}, t + 2);
+  // S = t % kStages; a compile-time constant in the unrolled main loop.
+  auto tile = [&](int S, int t, auto MASK_) {
+    const int SN = S + 1 < kStages ? S + 1 : 0;
     const bool tt = t == ptiles;
     const int nk = tt ? T : min(kTile, npk - t * kTile);  // real keys of this tile
-    block(S_, I0{}, min(nk, 32), tt);
-    if (nk > 32) block(S_, I1{}, nk - 32, tt);
-    if (t + 1 < ntiles) {
+    const bool more = t + 1 < ntiles;
+    // both blocks always run: a block without real keys (the last tile may
+    // hold 32 or fewer) is fully masked, its probabilities are zero
+    qk_softmax(I0{}, min(nk, 32), tt, MASK_);
+    pv(S, I0{}, [&] { kload(S, I1{}); });
+    qk_softmax(I1{}, nk - 32, tt, MASK_);
+    if (more) {
       wait_own(min(1, ntiles - 2 - t));
-      convert(SN{});
+      convert(SN);
     }
+    lds_barrier();
+    if (t + 3 < ntiles) dma(S, t + 3);
+    // (after the last tile this reads a stage nobody uses; harmless, and it
+    // keeps the P.V free of branches)
+    pv(S, I1{}, [&] { kload(SN, I0{}); });
   };
   // Tile 0 alone first: every workgroup starts at once, and tile 0 arrives
-  // sooner when the loads of tile 1 are not competing with it.
-  dma(I0{}, 0);
+  // sooner when the loads of the next tiles are not competing with it.
+  dma(0, 0);
   wait_own(0);
-  if (ntiles > 1) dma(I1{}, 1);
-  convert(I0{});
-  for (int t = 0; t < ntiles; t += kStages) {
-    tile(I0{}, t);
-    if (t + 1 < ntiles) tile(I1{}, t + 1);
-    if (t + 2 < ntiles) tile(I2{}, t + 2);
+  if (ntiles > 1) dma(1, 1);
+  if (ntiles > 2) dma(2, 2);
+  convert(0);
+  lds_barrier();
+  kload(0, I0{});
+  // Full prefix tiles need no mask; the last prefix tile when partial and
+  // the tree tile run masked after them, with the stage a run-time value.
+  const int nfull = npk / kTile;
+  int t = 0;
+  for (; t + kStages <= nfull; t += kStages) {
+    tile(0, t, std::false_type{});
+    tile(1, t + 1, std::false_type{});
+    tile(2, t + 2, std::false_type{});
   }
+  for (; t < ntiles; ++t) tile(t % kStages, t, std::true_type{});
 
   // ---- normalise and write the partial.  A row of o = acc / l goes out as
   // int16 snorm values acc / max|acc| with the row's max|o| as its scale
@@ -538,7 +621,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.smem = smem;
   x.tid = threadIdx.x;
   x.lane = threadIdx.x & 63;
-  x.wave = threadIdx.x >> 6;
+  x.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar registers
   x.l16 = x.lane & 15;
   x.grp = x.lane >> 4;
   x.g = blockIdx.x;
