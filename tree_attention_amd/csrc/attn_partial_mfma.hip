@@ -238,8 +238,8 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   //         key: far above any real offset, so the first key moves the
   //         reference and scales the empty accumulator by 2^-kNoRef = 0,
   //         and masked scores still give 2^-inf = 0, never inf - inf),
-  //   thr   m + 8/c2 = -nmc/c2 + 8/c2, formed when needed: a score above it
-  //         would give a probability above 2^8,
+  //   thr   m + 15/c2 = -nmc/c2 + 15/c2, formed when needed: a score above
+  //         it would give a probability above 2^15 (fp16 holds up to 65504),
   //   lsum  sum of this lane's probabilities as rounded to fp16 for P.V (the
   //         output is normalised by the same values it accumulates).
   constexpr float kNoRef = 1e30f;
@@ -253,7 +253,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     for (int dt = 0; dt < C::DT; ++dt) acc[dt][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
   const float c2 = a.scale_log2;
-  const float t8 = a.headroom;             // 8 / c2
+  const float t8 = a.headroom;             // 15 / c2
   const float nic2 = a.neg_inv_scale_log2;  // -1 / c2
   auto thr = [&](int rt) { return fmaf(nmc[rt], nic2, t8); };
   // prefix tiles, then one tree tile (T <= 64)
@@ -452,21 +452,15 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const float alpha = up ? __builtin_amdgcn_exp2f(n_new - nmc[rt]) : 1.f;
     nmc[rt] = n_new;
     lsum[rt] *= alpha;
-    // The scaled accumulator goes back through an MFMA (0*0 + C) so that
-    // every definition of acc inside the loop is an MFMA result and acc
-    // stays in the accumulation registers.
-    const f16x8 z8 = __builtin_bit_cast(f16x8, (u32x4){0u, 0u, 0u, 0u});
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(z8, z8, acc[dt][rt] * alpha, 0, 0, 0);
-    }
+    for (int dt = 0; dt < C::DT; ++dt) acc[dt][rt] *= alpha;
   };
 
   // Online softmax in base 2, with a lazily moved reference max.  Each lane
   // checks its own eight scores of a row against the row threshold; only
-  // when some score would give a probability above 2^8 does the wave reduce
+  // when some score would give a probability above 2^15 does the wave reduce
   // the row maxima across lane groups, move the reference and rescale.
-  // Keeping probabilities up to 2^8 against a stale reference is exact: the
+  // Keeping probabilities up to 2^15 against a stale reference is exact: the
   // final normalisation and the lse use the same reference.
   //
   // Row tile by row tile: the check of row tile rt, then its exponentials

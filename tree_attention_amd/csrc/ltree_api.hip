@@ -167,7 +167,7 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
   a.slots = p.slots;
   a.max_prefix_len = p.max_prefix_len;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.headroom = 8.f / a.scale_log2;
+  a.headroom = 15.f / a.scale_log2;
   a.neg_inv_scale_log2 = -1.f / a.scale_log2;
 
   hipError_t err;

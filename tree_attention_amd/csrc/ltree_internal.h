@@ -54,7 +54,7 @@ struct PartialArgs {
   int chunk, max_chunks, slots, max_prefix_len;
   int rows_per_wg, row_blocks;
   float scale_log2;  // scale * log2(e)
-  float headroom;    // 8 / scale_log2: raw-score margin of the lazy softmax reference
+  float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
   float neg_inv_scale_log2;  // -1 / scale_log2
 };
 
