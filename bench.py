@@ -115,6 +115,81 @@ def cpu_baseline(w, budget_s=15.0):
     }
 
 
+def time_graph(fn, K):
+    """Microseconds per call of fn(s) (s = 0..K-1), K calls captured in one HIP
+    graph, after an untimed replay."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(K):
+            fn(s)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e6 / K
+
+
+def row_xattn(args):
+    """Draft cross-attention into the target's KV cache: the 64 query tokens of
+    the QwQ-shaped layer over its 32768-key prefix, no tree part
+    (ltree_prefix_attn; split-K partials + merge, the same kernels)."""
+    import math
+
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_config
+
+    w = make_config(4)
+    dev = "cuda:0"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_prefix.shape[1]
+    e = w.q.element_size()
+    L = sum(w.prefix_lens)
+    q, off = w.q.to(dev), w.offsets.to(dev)
+    kv_bytes = 2 * w.k_prefix.numel() * e
+    n = max(2, math.ceil(512e6 / kv_bytes))
+    kp0, vp0 = w.k_prefix.to(dev), w.v_prefix.to(dev)
+    kv = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(n - 1)]
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty((ta.ltree_attn_workspace_bytes(B, T, Hq, Hkv, D, L),), dtype=torch.uint8,
+                     device=dev)
+
+    def call(s):
+        kp, vp = kv[s % n]
+        return ta.ltree_prefix_attn(q, kp, vp, off, L, o, lse, ws, w.scale)
+
+    for s in range(args.warmup):
+        assert call(s) == 0
+    torch.cuda.synchronize()
+    us = time_graph(call, args.steps)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    flop = 4 * D * Hq * T * L
+    bytes_ = 2 * L * Hkv * D * e + B * T * Hq * D * e + B * T * Hq * D * 4 + B * Hq * T * 4
+    tflops = flop / (us * 1e-6) / 1e12
+    return {
+        "metric": "draft cross-attention into the target KV cache, µs/call + TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), 1% of prefix rows x8)",
+        "config": {"workload": "draft-xattn-qwq32b-gqa40/8-d128-L32k-T64", "B": B, "T": T,
+                   "Hq": Hq, "Hkv": Hkv, "D": D, "prefix_lens": w.prefix_lens,
+                   "cache": f"cold ({n} rotating KV copies)"},
+        "us_per_call": round(us, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "hbm_frac": round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+
+
+ROWS = {"xattn": row_xattn}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +200,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-MiB buffer 5 times (calibrates HBM byte counters)")
+    ap.add_argument("--row", choices=sorted(ROWS), default=None,
+                    help="measure one of the steps around the verification path instead")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -149,6 +226,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
+        return
+    if args.row:
+        print(json.dumps(ROWS[args.row](args)), flush=True)
         return
     spec = CONFIGS[args.config]
     log(f"generating workload {spec['name']}")

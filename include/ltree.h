@@ -176,6 +176,28 @@ int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
                      float* o, float* lse, const void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * ltree_prefix_attn -- attention of T query tokens over the prefix KV cache
+ * alone, no mask and no tree part: the draft model's cross-attention into the
+ * target model's shared KV cache (gist.science page, section 2 "Methodik",
+ * part A, item "Cross-Attention mit geteiltem KV-Cache": the draft reads the
+ * target's cache directly).  The same kernels as ltree_attn (split-K partials,
+ * then the log-sum-exp merge) with the tree part left out.
+ *
+ *   dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix, prefix_offsets,
+ *   max_prefix_len, o, lse, workspace, workspace_bytes, stream
+ *                  as for ltree_attn; T (1..64) counts the query tokens.  The
+ *                  workspace size is ltree_attn_workspace_bytes(B, T, Hq, Hkv,
+ *                  D, max_prefix_len).
+ *   A sequence with L_b = 0 has no key: its rows get o = 0 and lse = -inf.
+ *
+ * Returns as ltree_attn.  Two kernel launches.
+ */
+int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                      const void* q, const void* k_prefix, const void* v_prefix,
+                      const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,6 +16,9 @@ worked example):
   results are joined with a log-sum-exp step.
 * same page, section 1 "Problemstellung", item "Ineffiziente Verifikation":
   tree attention needs a mask over the draft tokens.
+* same page, section 2 "Methodik", part A, item "Cross-Attention mit
+  geteiltem KV-Cache": the draft model attends to the target model's KV cache
+  directly (the prefix-only attention of ``oracle_prefix_attn``).
 * mlsanity.com, "LongSpec: Long-Context Lossless Speculative Decoding with
   Efficient Drafting and Verification", section "Abstract (arXiv)": fast
   prefix computation is combined with standard tree attention.
@@ -33,5 +36,6 @@ from .tree_attention_oracle import (  # noqa: F401
     oracle_attn_rows,
     oracle_attn_split,
     oracle_mask,
+    oracle_prefix_attn,
     tree_depth,
 )

@@ -28,6 +28,9 @@ Citations are by page title and section:
   Verifikation": verification of a speculation tree uses a tree-attention mask.
 * [ARXIV-ABS] mlsanity.com page of the same paper, section "Abstract
   (arXiv)": fast prefix computation combined with standard tree attention.
+* [GIST-2A] the gist.science page, section 2 "Methodik", part A, item
+  "Cross-Attention mit geteiltem KV-Cache": the draft model reads the target
+  model's KV cache directly.
 
 Readings where the pages are silent (each is listed in the design doc):
 
@@ -53,6 +56,7 @@ __all__ = [
     "oracle_attn_rows",
     "oracle_attn_split",
     "lse_merge",
+    "oracle_prefix_attn",
 ]
 
 
@@ -277,3 +281,42 @@ def oracle_attn_split(q, k_prefix, v_prefix, offsets, k_tree, v_tree, parent,
     o_m, lse_m = lse_merge(parts)
     return ((o_p, lse_p), (o_t, lse_t),
             (np.transpose(o_m, (0, 2, 1, 3)), lse_m))
+
+
+# --------------------------------------------------------------------------
+# Draft cross-attention into the target's KV cache ([GIST-2A])
+# --------------------------------------------------------------------------
+
+def oracle_prefix_attn(q, k_prefix, v_prefix, offsets, scale):
+    """Attention of T query tokens over the prefix keys alone, no mask.
+
+    gist.science page, section 2 "Methodik", part A, item "Cross-Attention mit
+    geteiltem KV-Cache": the draft model attends directly to the target
+    model's KV cache.  q [B,T,Hq,D]; k_prefix, v_prefix [sum L_b, Hkv, D]
+    packed by `offsets` [B+1].  Returns fp64 o [B,T,Hq,D] and lse [B,Hq,T]
+    (natural log).  A sequence without prefix keys (L_b = 0) has an empty
+    softmax: o = 0 and lse = -inf (the reading of the empty cached part in
+    [GIST-2C], taken here for the whole call).
+    """
+    q = _f64(q)
+    kp, vp = _f64(k_prefix), _f64(v_prefix)
+    B, T, Hq, D = q.shape
+    Hkv = kp.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    G = Hq // Hkv
+    off = np.asarray(offsets, dtype=np.int64)
+    if off.shape != (B + 1,) or off[0] != 0 or np.any(np.diff(off) < 0):
+        raise ValueError("offsets must be [B+1], start at 0 and not decrease")
+    o = np.zeros((B, T, Hq, D))
+    lse = np.full((B, Hq, T), -np.inf)
+    for b in range(B):
+        if off[b + 1] == off[b]:
+            continue
+        for h in range(Hq):
+            keys = kp[off[b]:off[b + 1], h // G, :]
+            vals = vp[off[b]:off[b + 1], h // G, :]
+            s = (q[b, :, h, :] @ keys.T) * scale          # [T, L_b]
+            o[b, :, h, :], lse[b, h, :] = _masked_softmax_rows(
+                s, np.ones_like(s, dtype=bool), vals)
+    return o, lse

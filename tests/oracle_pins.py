@@ -371,4 +371,46 @@ def pin_bf16_inputs_exact(orc):
     assert np.array_equal(o, o2) and np.array_equal(lse, l2)
 
 
+# ------------------------------------------------- prefix-only attention
+
+def pin_prefix_attn_vs_sdpa(orc):
+    """Attention over the prefix alone == torch CPU fp64 SDPA without a mask
+    (GQA by repeating KV heads in contiguous groups), lse == scipy logsumexp;
+    an empty prefix gives o = 0 and lse = -inf."""
+    w = _case(31, B=3, T=5, Hq=6, Hkv=3, prefix_lens=(7, 0, 4))
+    o, lse = orc.oracle_prefix_attn(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(), w.scale)
+    off = w.offsets.numpy()
+    B, T, Hq, D = w.q.shape
+    G = Hq // w.k_prefix.shape[1]
+    for b in range(B):
+        if off[b + 1] == off[b]:
+            assert np.all(o[b] == 0) and np.all(lse[b] == -np.inf)
+            continue
+        k = w.k_prefix[off[b]:off[b + 1]].double().repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+        v = w.v_prefix[off[b]:off[b + 1]].double().repeat_interleave(G, dim=1).transpose(0, 1).contiguous()
+        q = w.q[b].double().transpose(0, 1).contiguous()
+        out = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=w.scale)
+        assert np.max(np.abs(o[b] - out.transpose(0, 1).numpy())) < TOL
+        s = (q @ k.transpose(1, 2)).numpy() * w.scale
+        assert np.max(np.abs(lse[b] - logsumexp(s, axis=-1))) < TOL
+
+
+def pin_prefix_attn_uniform_keys(orc):
+    """All prefix keys equal: o = mean of the sequence's values, lse = s0 + ln L."""
+    w = _case(32, B=2, T=3, Hq=4, Hkv=2, prefix_lens=(5, 2))
+    key = torch.randn(w.k_prefix.shape[-1], generator=torch.Generator().manual_seed(1))
+    kp = key.expand_as(w.k_prefix).clone()
+    o, lse = orc.oracle_prefix_attn(w.q, kp, w.v_prefix, w.offsets.numpy(), w.scale)
+    off = w.offsets.numpy()
+    for b in range(2):
+        L = int(off[b + 1] - off[b])
+        for h in range(4):
+            g = h // 2
+            mean = w.v_prefix[off[b]:off[b + 1], g].double().mean(0).numpy()
+            for i in range(3):
+                s0 = w.scale * float(w.q[b, i, h].double() @ key.double())
+                assert np.max(np.abs(o[b, i, h] - mean)) < TOL
+                assert abs(lse[b, h, i] - (s0 + math.log(L))) < TOL
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -31,6 +31,9 @@ MUTATIONS = {
     "parent_allows_self": ("if not (-1 <= int(p[b, i]) <= i - 1):", "if not (-1 <= int(p[b, i]) <= i):"),
     "merge_unnormalised": ("o = sum((w[k] / z)[..., None]", "o = sum((w[k])[..., None]"),
     "merge_lse_no_max": ("lse = m + np.log(z)\n", "lse = np.log(z)\n"),
+    "prefix_attn_wrong_head": ("            keys = kp[off[b]:off[b + 1], h // G, :]", "            keys = kp[off[b]:off[b + 1], h % Hkv, :]"),
+    "prefix_attn_values_from_keys": ("            vals = vp[off[b]:off[b + 1], h // G, :]", "            vals = kp[off[b]:off[b + 1], h // G, :]"),
+    "prefix_attn_scale_dropped": ("            s = (q[b, :, h, :] @ keys.T) * scale          # [T, L_b]", "            s = (q[b, :, h, :] @ keys.T)          # [T, L_b]"),
     "rows_wrong_head": ("        g = h // G\n        if (b, g) not in cache:", "        g = h % Hkv\n        if (b, g) not in cache:"),
 }
 

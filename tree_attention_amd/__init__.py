@@ -24,7 +24,9 @@ from ._binding import (  # noqa: F401
     ltree_attn_partials,
     ltree_attn_workspace_bytes,
     ltree_build_mask,
+    ltree_prefix_attn,
     ltree_status_string,
     ltree_version,
+    prefix_attn,
     workspace_for,
 )

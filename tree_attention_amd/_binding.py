@@ -30,7 +30,7 @@ LTREE_MAX_TREE = 64
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
-            "ltree_attn_merge")
+            "ltree_attn_merge", "ltree_prefix_attn")
 
 
 class LTreeError(RuntimeError):
@@ -42,7 +42,7 @@ class LTreeError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is not built; run `python -m tree_attention_amd.build` "
+            f"{_LIB_PATH} is not built; run `python tree_attention_amd/build.py` "
             "(hipcc, gfx950) first")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
@@ -54,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "ltree_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, P, P, S, P]),
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
+        "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -183,6 +184,32 @@ def ltree_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_
         _stream(stream))
 
 
+def ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, lse, workspace,
+                      scale, stream=None) -> int:
+    """q [B, T, Hq, D] over the prefix alone (no tree part); o, lse as ltree_attn."""
+    dt = q.dtype
+    for name, t in (("q", q), ("k_prefix", k_prefix), ("v_prefix", v_prefix)):
+        _dev(t, name, dt)
+    _dev(prefix_offsets, "prefix_offsets", torch.int32)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    B, T, Hq, D = q.shape
+    if k_prefix.dim() != 3 or k_prefix.shape[2] != D or v_prefix.shape != k_prefix.shape:
+        raise ValueError("k_prefix/v_prefix must be [sum L, Hkv, D]")
+    Hkv = k_prefix.shape[1]
+    if prefix_offsets.shape != (B + 1,):
+        raise ValueError("prefix_offsets must be [B+1]")
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    return _lib.ltree_prefix_attn(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
+        _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+
+
 # --------------------------------------------------- allocating conveniences
 
 def build_mask(parent, with_status=True, stream=None):
@@ -216,4 +243,23 @@ def attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree, 
                     mask, o, lse, workspace, scale, stream)
     if st != LTREE_OK:
         raise LTreeError(st, "ltree_attn")
+    return o, lse
+
+
+def prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, scale, workspace=None,
+                stream=None):
+    """Allocate o and lse and run ltree_prefix_attn (attention over the prefix alone)."""
+    B, T, Hq, D = q.shape
+    Hkv = k_prefix.shape[1]
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = ltree_attn_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len)
+        if n == 0:
+            raise LTreeError(LTREE_ERR_INVALID_ARG, "ltree_attn_workspace_bytes")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    st = ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, lse,
+                           workspace, scale, stream)
+    if st != LTREE_OK:
+        raise LTreeError(st, "ltree_prefix_attn")
     return o, lse

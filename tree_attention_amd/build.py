@@ -1,6 +1,8 @@
 """Build libltree.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m tree_attention_amd.build        # or tree_attention_amd.build.build()
+    python tree_attention_amd/build.py        # or __graft_entry__.build()
+
+(Run as a file: importing the package loads the library it builds.)
 """
 
 from __future__ import annotations

@@ -553,11 +553,15 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   };
   // Tile 0 alone first: every workgroup starts at once, and tile 0 arrives
   // sooner when the loads of the next tiles are not competing with it.
-  dma(0, 0);
-  wait_own(0);
-  if (ntiles > 1) dma(1, 1);
-  if (ntiles > 2) dma(2, 2);
-  convert(0);
+  // (no tile at all only for an empty prefix without tree keys: the partial
+  // is then empty, lse -inf)
+  if (ntiles > 0) {
+    dma(0, 0);
+    wait_own(0);
+    if (ntiles > 1) dma(1, 1);
+    if (ntiles > 2) dma(2, 2);
+    convert(0);
+  }
   lds_barrier();
   kload(0, I0{});
   // Full prefix tiles need no mask; the last prefix tile when partial and
@@ -599,7 +603,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       }
       if (grp == 0) {
         a.lse_part[pbase + r] = -nmc[rt] + __builtin_amdgcn_logf(l);
-        a.scale_part[pbase + r] = mx / l;
+        a.scale_part[pbase + r] = l > 0.f ? mx / l : 0.f;
       }
     }
   }
@@ -632,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   if (x.slot >= nparts) return;
   const int k0 = x.slot * a.chunk;
   x.npk = max(0, min(a.chunk, L - k0));
-  x.tree = x.slot == nparts - 1;
+  x.tree = a.has_tree && x.slot == nparts - 1;
   x.kstride = a.Hkv * D;
   const size_t row0 = static_cast<size_t>(off0) + k0;
   x.kbase = static_cast<const __bf16*>(a.kp) + (row0 * a.Hkv + x.g) * D;

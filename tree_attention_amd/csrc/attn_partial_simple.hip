@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   if (slot >= nparts) return;
   const int k0 = slot * a.chunk;
   const int npk = max(0, min(a.chunk, L - k0));
-  const bool tree = slot == nparts - 1;
+  const bool tree = a.has_tree && slot == nparts - 1;
   const size_t kstride = static_cast<size_t>(a.Hkv) * D;
   const Tin* kp = static_cast<const Tin*>(a.kp) + (static_cast<size_t>(off0 + k0) * a.Hkv + g) * D;
   const Tin* vp = static_cast<const Tin*>(a.vp) + (static_cast<size_t>(off0 + k0) * a.Hkv + g) * D;
@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
 
   if (!active) return;
   const size_t pr = (static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r;  // active row
-  const float inv = 1.f / l;
+  const float inv = l > 0.f ? 1.f / l : 0.f;  // no keys: o = 0, lse = -inf
   float* op = static_cast<float*>(a.o_part) + pr * D;
 #pragma unroll
   for (int d = 0; d < D; ++d) op[d] = acc[d] * inv;

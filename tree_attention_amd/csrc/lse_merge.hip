@@ -7,6 +7,9 @@
 // as several prefix splits (the last of which has also taken in the tree
 // keys), so the same merge reduces the splits.
 //
+// The same merge serves prefix-only attention (no tree part); a row whose
+// partials are all empty (empty prefix) gets o = 0 and lse = -inf.
+//
 // For one output row with partials (o_s, l_s), l_s = log2 of the partial sum:
 //   M = max_s l_s,  w_s = 2^(l_s - M),  Z = sum_s w_s,
 //   o = sum_s (w_s / Z) o_s,  lse = ln 2 * (M + log2 Z).
@@ -106,6 +109,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     if (s0 + j < nparts) mx = fmaxf(mx, lse_part[part_row(s0 + j)]);
   }
   mx = wave_max(mx);
+  if (mx == -INFINITY) {
+    // no key at all (prefix-only attention over an empty prefix): the
+    // softmax of an empty set, taken as o = 0 and lse = -inf
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) orow[f] = 0.f;
+    if (j == 0) *lrow = -INFINITY;
+    return;
+  }
   float z = 0.f;
   for (int s0 = 0; s0 < nparts; s0 += kBatch) {
     if (s0 + j < nparts) z += exp2f(lse_part[part_row(s0 + j)] - mx);

@@ -120,24 +120,25 @@ static int check_sizes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len)
   return LTREE_OK;
 }
 
-int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
-                        const void* q, const void* k_prefix, const void* v_prefix,
-                        const int32_t* prefix_offsets, int max_prefix_len, const void* k_tree,
-                        const void* v_tree, const uint64_t* mask, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+// Partials of prefix (+ tree, when has_tree) attention into the workspace.
+static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                    const void* q, const void* k_prefix, const void* v_prefix,
+                    const int32_t* prefix_offsets, int max_prefix_len, bool has_tree,
+                    const void* k_tree, const void* v_tree, const uint64_t* mask,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f)) return LTREE_ERR_INVALID_ARG;
-  if (q == nullptr || prefix_offsets == nullptr || k_tree == nullptr || v_tree == nullptr ||
-      mask == nullptr || workspace == nullptr) {
+  if (q == nullptr || prefix_offsets == nullptr || workspace == nullptr) return LTREE_ERR_INVALID_ARG;
+  if (has_tree && (k_tree == nullptr || v_tree == nullptr || mask == nullptr)) {
     return LTREE_ERR_INVALID_ARG;
   }
   if (max_prefix_len > 0 && (k_prefix == nullptr || v_prefix == nullptr)) {
     return LTREE_ERR_INVALID_ARG;
   }
   // 16-byte vector loads of q/k/v rows
-  if (!aligned(q, 16) || !aligned(k_tree, 16) || !aligned(v_tree, 16) ||
+  if (!aligned(q, 16) || (has_tree && (!aligned(k_tree, 16) || !aligned(v_tree, 16))) ||
       (k_prefix && !aligned(k_prefix, 16)) || (v_prefix && !aligned(v_prefix, 16))) {
     return LTREE_ERR_INVALID_ARG;
   }
@@ -169,6 +170,7 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
   a.scale_log2 = scale * 1.4426950408889634f;
   a.headroom = 15.f / a.scale_log2;
   a.neg_inv_scale_log2 = -1.f / a.scale_log2;
+  a.has_tree = has_tree ? 1 : 0;
 
   hipError_t err;
   if (dtype == LTREE_BF16) {
@@ -177,6 +179,15 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
     err = ltree::launch_partials_simple(dtype, p, a, stream);
   }
   return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
+}
+
+int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                        const void* q, const void* k_prefix, const void* v_prefix,
+                        const int32_t* prefix_offsets, int max_prefix_len, const void* k_tree,
+                        const void* v_tree, const uint64_t* mask, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  return partials(dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix, prefix_offsets,
+                  max_prefix_len, true, k_tree, v_tree, mask, workspace, workspace_bytes, stream);
 }
 
 int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
@@ -209,6 +220,19 @@ int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float sc
   int st = ltree_attn_partials(dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix,
                                prefix_offsets, max_prefix_len, k_tree, v_tree, mask, workspace,
                                workspace_bytes, stream);
+  if (st != LTREE_OK) return st;
+  return ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse,
+                          workspace, workspace_bytes, stream);
+}
+
+int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                      const void* q, const void* k_prefix, const void* v_prefix,
+                      const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (o == nullptr || lse == nullptr) return LTREE_ERR_INVALID_ARG;
+  int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix, prefix_offsets,
+                    max_prefix_len, false, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                    stream);
   if (st != LTREE_OK) return st;
   return ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse,
                           workspace, workspace_bytes, stream);

@@ -53,6 +53,7 @@ struct PartialArgs {
   int B, T, Hq, Hkv, G, R;
   int chunk, max_chunks, slots, max_prefix_len;
   int rows_per_wg, row_blocks;
+  int has_tree;      // 0: prefix keys only (no tree part; the tree arguments are unused)
   float scale_log2;  // scale * log2(e)
   float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
   float neg_inv_scale_log2;  // -1 / scale_log2
