@@ -187,7 +187,64 @@ def row_xattn(args):
     }
 
 
-ROWS = {"xattn": row_xattn}
+def row_commit(args):
+    """KV-cache commit of the accepted branch: 4 accepted tokens (about the
+    accepted length the pages report) of the QwQ-shaped 64-node tree appended
+    after the 32768-row prefix cache (ltree_commit_kv)."""
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_config
+
+    w = make_config(4)
+    dev = "cuda:0"
+    B, T, Hkv, D = w.k_tree.shape
+    e = w.k_tree.element_size()
+    parent = w.parent[0].tolist()
+    node = next(i for i in range(T) if sum(1 for _ in _walk(parent, i)) >= 4)
+    path = list(_walk(parent, node))[::-1][:4]
+    L = w.k_prefix.shape[0]
+    kc = torch.zeros((L + T, Hkv, D), dtype=w.k_tree.dtype, device=dev)
+    vc = torch.zeros_like(kc)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    acc = torch.zeros((B, T), dtype=torch.int32)
+    acc[0, :4] = torch.tensor(path, dtype=torch.int32)
+    acc = acc.to(dev)
+    n_acc = torch.tensor([4], dtype=torch.int32, device=dev)
+    dst = torch.tensor([L], dtype=torch.int32, device=dev)
+    status = torch.zeros((1,), dtype=torch.int32, device=dev)
+
+    def call(s):
+        return ta.ltree_commit_kv(kt, vt, acc, n_acc, dst, kc, vc, status)
+
+    for s in range(args.warmup):
+        assert call(s) == 0
+    torch.cuda.synchronize()
+    us = time_graph(call, args.steps)
+    assert int(status.item()) == 0
+    bytes_ = 2 * 2 * 4 * Hkv * D * e          # K and V rows, read and written
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return {
+        "metric": "KV-cache commit of the accepted branch, µs/call",
+        "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "commit-qwq32b-kv8-d128-T64-accept4", "B": B, "T": T, "Hkv": Hkv,
+                   "D": D, "accepted": 4, "cache_rows": L + T},
+        "us_per_call": round(us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 6), "traffic": None,
+                     "note": "32 KB moved per call: launch-latency bound"},
+    }
+
+
+def _walk(parent, i):
+    while i != -1:
+        yield i
+        i = parent[i]
+
+
+ROWS = {"xattn": row_xattn, "commit": row_commit}
 
 
 def main():

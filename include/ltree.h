@@ -198,6 +198,38 @@ int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
                       const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * ltree_commit_kv -- copy the keys and values of the accepted draft tokens from
+ * the tree buffers into the KV cache, so they join the cached prefix of the
+ * next verification step (gist.science page, opening explanation: the target
+ * keeps the proposals it accepts; section 3 "Wichtige Ergebnisse": about 3.5
+ * to 4 accepted tokens per pass).
+ *
+ *   dtype       element type of all four K/V arrays (LTREE_BF16 or LTREE_F32).
+ *   B, T, Hkv, D  1 <= T <= 64, D in {64, 128}.
+ *   k_tree, v_tree  [B, T, Hkv, D], as given to ltree_attn.
+ *   accepted    [B, T] int32: tree node ids of the accepted tokens of sequence
+ *               b in cache order (root side first); entries from n_accepted[b]
+ *               on are ignored.
+ *   n_accepted  [B] int32, 0 <= n <= T.
+ *   dst_row     [B] int32: cache row that takes accepted token 0 of sequence b;
+ *               tokens 1.. follow in consecutive rows.
+ *   k_cache, v_cache  [cache_rows, Hkv, D] in/out: rows dst_row[b] ..
+ *               dst_row[b] + n_accepted[b] - 1 are overwritten, nothing else.
+ *               Ranges of different sequences must not overlap.
+ *   status      [1] int32 out or NULL: 0, or 1 + the first sequence whose
+ *               n_accepted, dst_row or accepted ids are out of range; such a
+ *               sequence is not written.
+ *
+ * Returns LTREE_OK, LTREE_ERR_INVALID_ARG (null or misaligned pointer, bad
+ * sizes), LTREE_ERR_UNSUPPORTED or LTREE_ERR_HIP.  One kernel launch; all
+ * pointers 16-byte aligned.
+ */
+int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void* k_tree,
+                    const void* v_tree, const int32_t* accepted, const int32_t* n_accepted,
+                    const int32_t* dst_row, void* k_cache, void* v_cache, int cache_rows,
+                    int32_t* status, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,7 @@ from .tree_attention_oracle import (  # noqa: F401
     ancestor_matrix,
     check_parent,
     lse_merge,
+    oracle_commit_kv,
     oracle_attn,
     oracle_attn_rows,
     oracle_attn_split,

@@ -31,6 +31,9 @@ Citations are by page title and section:
 * [GIST-2A] the gist.science page, section 2 "Methodik", part A, item
   "Cross-Attention mit geteiltem KV-Cache": the draft model reads the target
   model's KV cache directly.
+* [GIST-INTRO] the gist.science page, opening explanation: the target model
+  keeps (writes down) the draft proposals it accepts; [GIST-3] its section 3
+  "Wichtige Ergebnisse": about 3.5 to 4 tokens are accepted per pass.
 
 Readings where the pages are silent (each is listed in the design doc):
 
@@ -57,6 +60,7 @@ __all__ = [
     "oracle_attn_split",
     "lse_merge",
     "oracle_prefix_attn",
+    "oracle_commit_kv",
 ]
 
 
@@ -320,3 +324,41 @@ def oracle_prefix_attn(q, k_prefix, v_prefix, offsets, scale):
             o[b, :, h, :], lse[b, h, :] = _masked_softmax_rows(
                 s, np.ones_like(s, dtype=bool), vals)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# KV-cache commit of the accepted draft tokens ([GIST-INTRO], [GIST-3])
+# --------------------------------------------------------------------------
+
+def oracle_commit_kv(k_tree, v_tree, accepted, n_accepted, dst_row, k_cache, v_cache):
+    """Copy the K/V rows of the accepted tree nodes into the cache.
+
+    For every sequence b whose arguments are in range, and j < n_accepted[b]:
+    cache row dst_row[b] + j takes tree row accepted[b, j] (all KV heads).
+    k_tree, v_tree [B,T,Hkv,D]; accepted [B,T] int; n_accepted, dst_row [B];
+    k_cache, v_cache [rows, Hkv, D] (not modified: copies are returned).
+
+    Returns (k_cache', v_cache', status) with status 0, or 1 + the first
+    sequence b with n_accepted[b] outside [0, T], an accepted id outside
+    [0, T) among its first n_accepted[b] entries, or a destination range
+    outside [0, rows); such a sequence is left unwritten.
+    """
+    kt, vt = np.asarray(k_tree), np.asarray(v_tree)
+    acc = np.asarray(accepted)
+    n_acc, dst = np.asarray(n_accepted), np.asarray(dst_row)
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    B, T = acc.shape
+    rows = kc.shape[0]
+    status = 0
+    for b in range(B):
+        n, d = int(n_acc[b]), int(dst[b])
+        ok = 0 <= n <= T and 0 <= d and d + n <= rows
+        ok = ok and all(0 <= int(acc[b, j]) < T for j in range(n))
+        if not ok:
+            if status == 0:
+                status = 1 + b
+            continue
+        for j in range(n):
+            kc[d + j] = kt[b, int(acc[b, j])]
+            vc[d + j] = vt[b, int(acc[b, j])]
+    return kc, vc, status

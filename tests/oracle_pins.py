@@ -413,4 +413,61 @@ def pin_prefix_attn_uniform_keys(orc):
                 assert abs(lse[b, h, i] - (s0 + math.log(L))) < TOL
 
 
+# ------------------------------------------------------------ KV commit
+
+def pin_commit_hand_example(orc):
+    """Two sequences, one of them accepting nothing, worked by hand."""
+    kt = np.arange(2 * 3 * 1 * 2, dtype=np.float32).reshape(2, 3, 1, 2)      # [B,T,Hkv,D]
+    vt = -kt
+    kc = np.full((6, 1, 2), 7.0, dtype=np.float32)
+    vc = np.full((6, 1, 2), 9.0, dtype=np.float32)
+    acc = np.array([[0, 2, 1], [1, 0, 0]], dtype=np.int32)
+    k2, v2, st = orc.oracle_commit_kv(kt, vt, acc, np.array([2, 0]), np.array([3, 0]), kc, vc)
+    assert st == 0
+    expect = np.full((6, 1, 2), 7.0, dtype=np.float32)
+    expect[3, 0] = [0.0, 1.0]     # tree row (b=0, node 0)
+    expect[4, 0] = [4.0, 5.0]     # tree row (b=0, node 2)
+    assert np.array_equal(k2, expect) and np.array_equal(v2[3:5], -expect[3:5])
+    assert np.all(v2[[0, 1, 2, 5]] == 9.0) and np.all(kc == 7.0)
+
+
+def pin_commit_chain_appends_tree(orc):
+    """Accepting a whole chain in order appends the tree rows unchanged; rows
+    outside the destination range keep their values."""
+    rng = np.random.default_rng(41)
+    kt = rng.standard_normal((2, 5, 3, 4))
+    vt = rng.standard_normal((2, 5, 3, 4))
+    kc = rng.standard_normal((20, 3, 4))
+    vc = rng.standard_normal((20, 3, 4))
+    acc = np.tile(np.arange(5, dtype=np.int32), (2, 1))
+    k2, v2, st = orc.oracle_commit_kv(kt, vt, acc, np.array([5, 5]), np.array([2, 11]), kc, vc)
+    assert st == 0
+    assert np.array_equal(k2[2:7], kt[0]) and np.array_equal(k2[11:16], kt[1])
+    assert np.array_equal(v2[2:7], vt[0]) and np.array_equal(v2[11:16], vt[1])
+    keep = [r for r in range(20) if not (2 <= r < 7 or 11 <= r < 16)]
+    assert np.array_equal(k2[keep], kc[keep]) and np.array_equal(v2[keep], vc[keep])
+
+
+def pin_commit_status(orc):
+    """Out-of-range arguments: the first bad sequence is reported and left
+    unwritten; good sequences are still written."""
+    kt = np.ones((3, 4, 1, 2))
+    kc = np.zeros((8, 1, 2))
+    acc = np.array([[0, 1, 2, 3], [0, 4, 0, 0], [3, 2, 0, 0]], dtype=np.int32)
+    # sequence 1 names node 4 of a 4-node tree
+    k2, _, st = orc.oracle_commit_kv(kt, kt, acc, np.array([1, 2, 2]), np.array([0, 2, 5]), kc, kc)
+    assert st == 2 and np.all(k2[0] == 1) and np.all(k2[2:4] == 0) and np.all(k2[5:7] == 1)
+    # destination past the end, and a negative count
+    _, _, st = orc.oracle_commit_kv(kt, kt, acc, np.array([1, 0, 2]), np.array([0, 0, 7]), kc, kc)
+    assert st == 3
+    _, _, st = orc.oracle_commit_kv(kt, kt, acc, np.array([-1, 0, 0]), np.array([0, 0, 0]), kc, kc)
+    assert st == 1
+    # an id past n_accepted is ignored
+    _, _, st = orc.oracle_commit_kv(kt, kt, acc, np.array([1, 1, 0]), np.array([0, 1, 2]), kc, kc)
+    assert st == 0
+    # a range ending exactly at the last cache row fits
+    k2, _, st = orc.oracle_commit_kv(kt, kt, acc, np.array([0, 0, 2]), np.array([0, 0, 6]), kc, kc)
+    assert st == 0 and np.all(k2[6:8] == 1)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

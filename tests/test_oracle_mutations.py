@@ -34,6 +34,9 @@ MUTATIONS = {
     "prefix_attn_wrong_head": ("            keys = kp[off[b]:off[b + 1], h // G, :]", "            keys = kp[off[b]:off[b + 1], h % Hkv, :]"),
     "prefix_attn_values_from_keys": ("            vals = vp[off[b]:off[b + 1], h // G, :]", "            vals = kp[off[b]:off[b + 1], h // G, :]"),
     "prefix_attn_scale_dropped": ("            s = (q[b, :, h, :] @ keys.T) * scale          # [T, L_b]", "            s = (q[b, :, h, :] @ keys.T)          # [T, L_b]"),
+    "commit_wrong_source": ("            kc[d + j] = kt[b, int(acc[b, j])]", "            kc[d + j] = kt[b, j]"),
+    "commit_off_by_one": ("        ok = 0 <= n <= T and 0 <= d and d + n <= rows", "        ok = 0 <= n <= T and 0 <= d and d + n < rows"),
+    "commit_values_from_keys": ("            vc[d + j] = vt[b, int(acc[b, j])]", "            vc[d + j] = kt[b, int(acc[b, j])]"),
     "rows_wrong_head": ("        g = h // G\n        if (b, g) not in cache:", "        g = h % Hkv\n        if (b, g) not in cache:"),
 }
 

@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     ltree_attn_partials,
     ltree_attn_workspace_bytes,
     ltree_build_mask,
+    ltree_commit_kv,
     ltree_prefix_attn,
     ltree_status_string,
     ltree_version,

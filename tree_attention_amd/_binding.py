@@ -30,7 +30,7 @@ LTREE_MAX_TREE = 64
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
-            "ltree_attn_merge", "ltree_prefix_attn")
+            "ltree_attn_merge", "ltree_prefix_attn", "ltree_commit_kv")
 
 
 class LTreeError(RuntimeError):
@@ -55,6 +55,7 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
         "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
+        "ltree_commit_kv": (I, [I, I, I, I, I, P, P, P, P, P, P, P, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -208,6 +209,29 @@ def ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, 
         _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
         _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def ltree_commit_kv(k_tree, v_tree, accepted, n_accepted, dst_row, k_cache, v_cache,
+                    status=None, stream=None) -> int:
+    """Copy accepted tree rows into the cache: k_cache[dst_row[b] + j] =
+    k_tree[b, accepted[b, j]] for j < n_accepted[b] (same for v)."""
+    dt = k_tree.dtype
+    for name, t in (("k_tree", k_tree), ("v_tree", v_tree), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        _dev(t, name, dt)
+    for name, t in (("accepted", accepted), ("n_accepted", n_accepted), ("dst_row", dst_row)):
+        _dev(t, name, torch.int32)
+    _dev(status, "status", torch.int32)
+    B, T, Hkv, D = k_tree.shape
+    if v_tree.shape != k_tree.shape or accepted.shape != (B, T) or n_accepted.shape != (B,) \
+            or dst_row.shape != (B,):
+        raise ValueError("k_tree/v_tree [B,T,Hkv,D], accepted [B,T], n_accepted/dst_row [B]")
+    if k_cache.dim() != 3 or k_cache.shape[1:] != (Hkv, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache/v_cache must be [rows, Hkv, D]")
+    return _lib.ltree_commit_kv(
+        _dtype_code(k_tree), B, T, Hkv, D, _ptr(k_tree), _ptr(v_tree), _ptr(accepted),
+        _ptr(n_accepted), _ptr(dst_row), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+        _ptr(status), _stream(stream))
 
 
 # --------------------------------------------------- allocating conveniences

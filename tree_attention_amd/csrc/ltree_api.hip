@@ -238,4 +238,30 @@ int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
                           workspace, workspace_bytes, stream);
 }
 
+int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void* k_tree,
+                    const void* v_tree, const int32_t* accepted, const int32_t* n_accepted,
+                    const int32_t* dst_row, void* k_cache, void* v_cache, int cache_rows,
+                    int32_t* status, hipStream_t stream) {
+  if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || Hkv < 1 || cache_rows < 0) return LTREE_ERR_INVALID_ARG;
+  if (T > LTREE_MAX_TREE || (D != 64 && D != 128)) return LTREE_ERR_UNSUPPORTED;
+  if (k_tree == nullptr || v_tree == nullptr || accepted == nullptr || n_accepted == nullptr ||
+      dst_row == nullptr || k_cache == nullptr || v_cache == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (!aligned(k_tree, 16) || !aligned(v_tree, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16)) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  const long row_bytes = static_cast<long>(Hkv) * D * (dtype == LTREE_BF16 ? 2 : 4);
+  // byte offsets of tree rows and cache rows stay below 2^63; the row itself
+  // is addressed with an int
+  if (row_bytes > (1L << 30) || static_cast<long>(B) * T > (1L << 30)) return LTREE_ERR_UNSUPPORTED;
+  return ltree::launch_kv_commit(k_tree, v_tree, accepted, n_accepted, dst_row, k_cache,
+                                 v_cache, B, T, static_cast<int>(row_bytes), cache_rows, status,
+                                 stream) == hipSuccess
+             ? LTREE_OK
+             : LTREE_ERR_HIP;
+}
+
 }  // extern "C"

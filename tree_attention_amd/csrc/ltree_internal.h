@@ -69,6 +69,11 @@ hipError_t launch_partials_mfma(const Plan& plan, PartialArgs args, hipStream_t 
 hipError_t launch_partials_simple(ltree_dtype dtype, const Plan& plan, PartialArgs args,
                                   hipStream_t stream);
 
+hipError_t launch_kv_commit(const void* k_tree, const void* v_tree, const int32_t* accepted,
+                            const int32_t* n_accepted, const int32_t* dst_row, void* k_cache,
+                            void* v_cache, int B, int T, int row_bytes, int cache_rows,
+                            int32_t* status, hipStream_t stream);
+
 // snorm: o_part holds int16 snorm values with per-row scales (bf16 path).
 hipError_t launch_merge(const Plan& plan, bool snorm, const int32_t* offsets, const void* o_part,
                         const float* scale_part, const float* lse_part, float* o, float* lse,
