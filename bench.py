@@ -244,7 +244,48 @@ def _walk(parent, i):
         i = parent[i]
 
 
-ROWS = {"xattn": row_xattn, "commit": row_commit}
+def row_rope(args):
+    """Rotary position embedding of the QwQ-shaped tree's queries and keys at
+    their tree positions after the 32768-key prefix (ltree_tree_rope)."""
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_config
+
+    w = make_config(4)
+    dev = "cuda:0"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    e = w.q.element_size()
+    q, kt = w.q.to(dev), w.k_tree.to(dev)
+    off = w.offsets.to(dev)
+    mask, _ = ta.build_mask(w.parent.to(dev))
+
+    def call(s):
+        return ta.ltree_tree_rope(q, kt, mask, off, 1e6)
+
+    for s in range(args.warmup):
+        assert call(s) == 0
+    torch.cuda.synchronize()
+    us = time_graph(call, args.steps)
+    bytes_ = 2 * B * T * (Hq + Hkv) * D * e + B * T * 8 + 4 * (B + 1)
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return {
+        "metric": "tree-position RoPE of tree Q/K, µs/call",
+        "value": round(us, 3), "unit": "us", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000, 6), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 (fp64 arithmetic)",
+        "data": "synthetic",
+        "config": {"workload": "rope-qwq32b-gqa40/8-d128-T64", "B": B, "T": T, "Hq": Hq,
+                   "Hkv": Hkv, "D": D, "rope_base": 1e6},
+        "us_per_call": round(us, 3),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 6), "traffic": None,
+                     "note": "786 KB moved per call: launch-latency bound"},
+    }
+
+
+ROWS = {"xattn": row_xattn, "commit": row_commit, "rope": row_rope}
 
 
 def main():

@@ -230,6 +230,33 @@ int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void*
                     const int32_t* dst_row, void* k_cache, void* v_cache, int cache_rows,
                     int32_t* status, hipStream_t stream);
 
+/*
+ * ltree_tree_rope -- rotary position embedding of the tree tokens, in place, at
+ * their tree positions (gist.science page, section 1 "Problemstellung", item
+ * "Trainings-Inferenz-Diskrepanz": positions enter through RoPE and must agree
+ * with the target model's; the mlsanity.com page lists RoFormer among the
+ * paper's references).  Node i of sequence b takes position
+ * p = L_b + depth(i) - 1, depth = popcount(mask row) (root = 1), so a token
+ * continues the prefix along its own branch and siblings share a position.
+ * For every head and k < D/2, with a = p * rope_base^(-2k/D):
+ *   x[k]       <- x[k] cos a - x[k + D/2] sin a
+ *   x[k + D/2] <- x[k + D/2] cos a + x[k] sin a
+ * evaluated in fp64 and rounded to nearest even into the storage type.
+ *
+ *   dtype          LTREE_BF16 or LTREE_F32, the type of q and k_tree.
+ *   q              [B, T, Hq, D] in/out.   k_tree  [B, T, Hkv, D] in/out.
+ *   mask           [B, T] uint64 from ltree_build_mask.  A zero row (a tree
+ *                  with an invalid parent) leaves that token unrotated.
+ *   prefix_offsets [B+1] int32 as for ltree_attn (L_b = o[b+1] - o[b]).
+ *   rope_base      > 1, the rotary base of the target model.
+ *
+ * Returns LTREE_OK, LTREE_ERR_INVALID_ARG, LTREE_ERR_UNSUPPORTED (T > 64,
+ * D not 64/128) or LTREE_ERR_HIP.  One kernel launch; run it before ltree_attn.
+ */
+int ltree_tree_rope(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, void* q,
+                    void* k_tree, const uint64_t* mask, const int32_t* prefix_offsets,
+                    double rope_base, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,5 +38,7 @@ from .tree_attention_oracle import (  # noqa: F401
     oracle_attn_split,
     oracle_mask,
     oracle_prefix_attn,
+    oracle_tree_rope,
+    round_bf16,
     tree_depth,
 )

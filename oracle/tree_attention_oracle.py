@@ -31,6 +31,10 @@ Citations are by page title and section:
 * [GIST-2A] the gist.science page, section 2 "Methodik", part A, item
   "Cross-Attention mit geteiltem KV-Cache": the draft model reads the target
   model's KV cache directly.
+* [GIST-1P] the gist.science page, section 1 "Problemstellung", item
+  "Trainings-Inferenz-Diskrepanz": positions enter through RoPE and the draft's
+  positions must agree with the target's; [MLS-REF] the mlsanity.com page
+  lists RoFormer (rotary position embedding) among the paper's references.
 * [GIST-INTRO] the gist.science page, opening explanation: the target model
   keeps (writes down) the draft proposals it accepts; [GIST-3] its section 3
   "Wichtige Ergebnisse": about 3.5 to 4 tokens are accepted per pass.
@@ -61,6 +65,8 @@ __all__ = [
     "lse_merge",
     "oracle_prefix_attn",
     "oracle_commit_kv",
+    "oracle_tree_rope",
+    "round_bf16",
 ]
 
 
@@ -362,3 +368,41 @@ def oracle_commit_kv(k_tree, v_tree, accepted, n_accepted, dst_row, k_cache, v_c
             kc[d + j] = kt[b, int(acc[b, j])]
             vc[d + j] = vt[b, int(acc[b, j])]
     return kc, vc, status
+
+
+# --------------------------------------------------------------------------
+# Rotary position embedding at tree positions ([GIST-1P], [MLS-REF])
+# --------------------------------------------------------------------------
+
+def oracle_tree_rope(q, k_tree, parent, offsets, base):
+    """Rotate the tree tokens' queries and keys to their tree positions.
+
+    Node i of sequence b sits at p = L_b + depth(i) - 1 (a token continues the
+    prefix along its own branch; root depth 1).  Channel pairs (k, k + D/2),
+    k < D/2, are rotated by p * base^(-2k/D): written here as the complex
+    product (x[k] + i x[k + D/2]) * exp(i p theta_k).  q [B,T,Hq,D],
+    k_tree [B,T,Hkv,D]; returns fp64 copies (unrounded).
+    """
+    q = _f64(q).copy()
+    kt = _f64(k_tree).copy()
+    B, T, Hq, D = q.shape
+    off = np.asarray(offsets, dtype=np.int64)
+    depth = tree_depth(parent)                        # [B, T]
+    half = D // 2
+    theta = np.power(float(base), -2.0 * np.arange(half) / D)
+    for b in range(B):
+        L = int(off[b + 1] - off[b])
+        for i in range(T):
+            rot = np.exp(1j * (L + depth[b, i] - 1) * theta)          # [D/2]
+            for x in (q[b, i], kt[b, i]):                             # [H, D] views
+                z = (x[:, :half] + 1j * x[:, half:]) * rot
+                x[:, :half], x[:, half:] = z.real, z.imag
+    return q, kt
+
+
+def round_bf16(x):
+    """fp64 values rounded to the nearest bf16 value (8 significant bits, ties
+    to even), returned as fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                                # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.rint(m * 256.0) / 256.0, e)    # np.rint: ties to even

@@ -470,4 +470,73 @@ def pin_commit_status(orc):
     assert st == 0 and np.all(k2[6:8] == 1)
 
 
+# ------------------------------------------------------------ tree RoPE
+
+def _rope_case(seed, trees, lens, D=8, Hq=4, Hkv=2, T=6):
+    rng = np.random.default_rng(seed)
+    return make_workload(rng, B=len(lens), T=T, Hq=Hq, Hkv=Hkv, D=D, prefix_lens=list(lens),
+                         trees=trees, dtype="f32")
+
+
+def pin_rope_position_zero_is_identity(orc):
+    """Roots of a forest over an empty prefix sit at position 0: unchanged;
+    every rotation keeps each channel pair's length."""
+    w = _rope_case(51, "forest", (0,))
+    q, k = orc.oracle_tree_rope(w.q, w.k_tree, w.parent.numpy(), w.offsets.numpy(), 10000.0)
+    roots = np.where(w.parent.numpy()[0] == -1)[0]
+    assert np.array_equal(q[0, roots], w.q[0, roots].double().numpy())
+    assert np.array_equal(k[0, roots], w.k_tree[0, roots].double().numpy())
+    for x, x0 in ((q, w.q), (k, w.k_tree)):
+        x0 = x0.double().numpy()
+        h = x.shape[-1] // 2
+        assert np.max(np.abs(np.hypot(x[..., :h], x[..., h:]) - np.hypot(x0[..., :h], x0[..., h:]))) < 1e-12
+
+
+def pin_rope_chain_positions_and_complex_rotation(orc):
+    """A chain after a prefix of 5: node i sits at 5 + i; each pair (k, k+D/2)
+    turns by (5 + i) * base^(-2k/D), checked with numpy's complex exponential
+    and, for k = 0 (angle = position), with math.cos / math.sin."""
+    w = _rope_case(52, "chain", (5,), D=4)
+    base = 500.0
+    q, _ = orc.oracle_tree_rope(w.q, w.k_tree, w.parent.numpy(), w.offsets.numpy(), base)
+    x = w.q.double().numpy()
+    for i in range(6):
+        p = 5 + i
+        c, s_ = math.cos(p), math.sin(p)
+        assert np.allclose(q[0, i, :, 0], x[0, i, :, 0] * c - x[0, i, :, 2] * s_, rtol=0, atol=1e-12)
+        assert np.allclose(q[0, i, :, 2], x[0, i, :, 2] * c + x[0, i, :, 0] * s_, rtol=0, atol=1e-12)
+        z = (x[0, i, :, 1] + 1j * x[0, i, :, 3]) * np.exp(1j * p * base ** -0.5)
+        assert np.allclose(q[0, i, :, 1], z.real, rtol=0, atol=1e-12)
+        assert np.allclose(q[0, i, :, 3], z.imag, rtol=0, atol=1e-12)
+
+
+def pin_rope_relative_positions(orc):
+    """Scores depend on position differences only: shifting every position by a
+    longer prefix leaves every query-key dot product of a sequence unchanged,
+    and siblings (same position) score a shared key alike."""
+    w = _rope_case(53, ("bounded", 3, 3), (7,), D=16, T=9)
+    w2 = _rope_case(53, ("bounded", 3, 3), (7,), D=16, T=9)
+    off_long = np.array([0, 1007])
+    q1, k1 = orc.oracle_tree_rope(w.q, w.k_tree, w.parent.numpy(), w.offsets.numpy(), 10000.0)
+    q2, k2 = orc.oracle_tree_rope(w2.q, w2.k_tree, w2.parent.numpy(), off_long, 10000.0)
+    G = 2
+    for h in range(4):
+        s1 = q1[0, :, h] @ k1[0, :, h // G].T
+        s2 = q2[0, :, h] @ k2[0, :, h // G].T
+        assert np.max(np.abs(s1 - s2)) < 1e-9
+
+
+def pin_round_bf16(orc):
+    """Against torch's fp32 -> bf16 conversion (round to nearest even) on fp32
+    values, ties included."""
+    rng = np.random.default_rng(54)
+    x = rng.standard_normal(4096).astype(np.float32)
+    # exact ties: bf16 values plus half an ulp
+    t = torch.tensor(x).to(torch.bfloat16).float().numpy()
+    ties = (t.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    for v in (x, ties):
+        ref = torch.tensor(v).to(torch.bfloat16).double().numpy()
+        assert np.array_equal(orc.round_bf16(v.astype(np.float64)), ref)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

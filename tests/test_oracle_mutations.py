@@ -37,6 +37,11 @@ MUTATIONS = {
     "commit_wrong_source": ("            kc[d + j] = kt[b, int(acc[b, j])]", "            kc[d + j] = kt[b, j]"),
     "commit_off_by_one": ("        ok = 0 <= n <= T and 0 <= d and d + n <= rows", "        ok = 0 <= n <= T and 0 <= d and d + n < rows"),
     "commit_values_from_keys": ("            vc[d + j] = vt[b, int(acc[b, j])]", "            vc[d + j] = kt[b, int(acc[b, j])]"),
+    "rope_position_off_by_one": ("            rot = np.exp(1j * (L + depth[b, i] - 1) * theta)", "            rot = np.exp(1j * (L + depth[b, i]) * theta)"),
+    "rope_adjacent_pairs": ("                z = (x[:, :half] + 1j * x[:, half:]) * rot", "                z = (x[:, 0::2] + 1j * x[:, 1::2]) * rot"),
+    "rope_theta_exponent": ("    theta = np.power(float(base), -2.0 * np.arange(half) / D)", "    theta = np.power(float(base), -1.0 * np.arange(half) / D)"),
+    "rope_q_only_for_k": ("            for x in (q[b, i], kt[b, i]):", "            for x in (q[b, i],):"),
+    "round_ties_away": ("    return np.ldexp(np.rint(m * 256.0) / 256.0, e)", "    return np.ldexp(np.floor(m * 256.0 + 0.5) / 256.0, e)"),
     "rows_wrong_head": ("        g = h // G\n        if (b, g) not in cache:", "        g = h % Hkv\n        if (b, g) not in cache:"),
 }
 

@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     ltree_commit_kv,
     ltree_prefix_attn,
     ltree_status_string,
+    ltree_tree_rope,
     ltree_version,
     prefix_attn,
     workspace_for,

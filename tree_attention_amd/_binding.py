@@ -30,7 +30,7 @@ LTREE_MAX_TREE = 64
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
-            "ltree_attn_merge", "ltree_prefix_attn", "ltree_commit_kv")
+            "ltree_attn_merge", "ltree_prefix_attn", "ltree_commit_kv", "ltree_tree_rope")
 
 
 class LTreeError(RuntimeError):
@@ -56,6 +56,7 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
         "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
         "ltree_commit_kv": (I, [I, I, I, I, I, P, P, P, P, P, P, P, I, P, P]),
+        "ltree_tree_rope": (I, [I, I, I, I, I, I, P, P, P, P, ctypes.c_double, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -232,6 +233,23 @@ def ltree_commit_kv(k_tree, v_tree, accepted, n_accepted, dst_row, k_cache, v_ca
         _dtype_code(k_tree), B, T, Hkv, D, _ptr(k_tree), _ptr(v_tree), _ptr(accepted),
         _ptr(n_accepted), _ptr(dst_row), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
         _ptr(status), _stream(stream))
+
+
+def ltree_tree_rope(q, k_tree, mask, prefix_offsets, rope_base, stream=None) -> int:
+    """Rotate q [B,T,Hq,D] and k_tree [B,T,Hkv,D] in place to the tree positions
+    L_b + depth(i) - 1 (depth = popcount of the mask row)."""
+    _dev(q, "q")
+    _dev(k_tree, "k_tree", q.dtype)
+    _dev(mask, "mask", torch.int64)
+    _dev(prefix_offsets, "prefix_offsets", torch.int32)
+    B, T, Hq, D = q.shape
+    if k_tree.dim() != 4 or k_tree.shape[:2] != (B, T) or k_tree.shape[3] != D:
+        raise ValueError("k_tree must be [B, T, Hkv, D]")
+    if mask.shape != (B, T) or prefix_offsets.shape != (B + 1,):
+        raise ValueError("mask must be [B, T] and prefix_offsets [B+1]")
+    return _lib.ltree_tree_rope(_dtype_code(q), B, T, Hq, k_tree.shape[2], D, _ptr(q),
+                                _ptr(k_tree), _ptr(mask), _ptr(prefix_offsets),
+                                float(rope_base), _stream(stream))
 
 
 # --------------------------------------------------- allocating conveniences

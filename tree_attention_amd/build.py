@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libltree.so")
 
 SOURCES = ["ltree_api.hip", "mask_build.hip", "attn_partial_mfma.hip",
-           "attn_partial_simple.hip", "lse_merge.hip", "kv_commit.hip"]
+           "attn_partial_simple.hip", "lse_merge.hip", "kv_commit.hip",
+           "tree_rope.hip"]
 
 # Packed fp32 VALU instructions are switched off: the compiler would otherwise
 # form v_pk_* ops from ordinary float code.  The host pass warns that it does

@@ -264,4 +264,21 @@ int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void*
              : LTREE_ERR_HIP;
 }
 
+int ltree_tree_rope(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, void* q,
+                    void* k_tree, const uint64_t* mask, const int32_t* prefix_offsets,
+                    double rope_base, hipStream_t stream) {
+  if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
+  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1) return LTREE_ERR_INVALID_ARG;
+  if (T > LTREE_MAX_TREE || (D != 64 && D != 128)) return LTREE_ERR_UNSUPPORTED;
+  if (!(std::isfinite(rope_base) && rope_base > 1.0)) return LTREE_ERR_INVALID_ARG;
+  if (q == nullptr || k_tree == nullptr || mask == nullptr || prefix_offsets == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (static_cast<long>(B) * T * (Hq + Hkv) * D > (1L << 40)) return LTREE_ERR_UNSUPPORTED;
+  return ltree::launch_tree_rope(dtype == LTREE_BF16, q, k_tree, mask, prefix_offsets, B, T, Hq,
+                                 Hkv, D, rope_base, stream) == hipSuccess
+             ? LTREE_OK
+             : LTREE_ERR_HIP;
+}
+
 }  // extern "C"

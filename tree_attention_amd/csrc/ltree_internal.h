@@ -74,6 +74,10 @@ hipError_t launch_kv_commit(const void* k_tree, const void* v_tree, const int32_
                             void* v_cache, int B, int T, int row_bytes, int cache_rows,
                             int32_t* status, hipStream_t stream);
 
+hipError_t launch_tree_rope(bool bf16, void* q, void* k_tree, const uint64_t* mask,
+                            const int32_t* offsets, int B, int T, int Hq, int Hkv, int D,
+                            double base, hipStream_t stream);
+
 // snorm: o_part holds int16 snorm values with per-row scales (bf16 path).
 hipError_t launch_merge(const Plan& plan, bool snorm, const int32_t* offsets, const void* o_part,
                         const float* scale_part, const float* lse_part, float* o, float* lse,
