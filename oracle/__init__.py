@@ -18,7 +18,9 @@ worked example):
   tree attention needs a mask over the draft tokens.
 * same page, section 2 "Methodik", part A, item "Cross-Attention mit
   geteiltem KV-Cache": the draft model attends to the target model's KV cache
-  directly (the prefix-only attention of ``oracle_prefix_attn``).
+  directly (the prefix-only attention of ``oracle_prefix_attn``); item
+  "Sliding-Window Self-Attention": the draft's own self-attention sees a
+  window of recent tokens (``oracle_window_attn``).
 * mlsanity.com, "LongSpec: Long-Context Lossless Speculative Decoding with
   Efficient Drafting and Verification", section "Abstract (arXiv)": fast
   prefix computation is combined with standard tree attention.
@@ -39,6 +41,7 @@ from .tree_attention_oracle import (  # noqa: F401
     oracle_mask,
     oracle_prefix_attn,
     oracle_tree_rope,
+    oracle_window_attn,
     round_bf16,
     tree_depth,
 )

@@ -35,11 +35,14 @@ Citations are by page title and section:
   "Trainings-Inferenz-Diskrepanz": positions enter through RoPE and the draft's
   positions must agree with the target's; [MLS-REF] the mlsanity.com page
   lists RoFormer (rotary position embedding) among the paper's references.
+* [GIST-2AW] the gist.science page, section 2 "Methodik", part A, item
+  "Sliding-Window Self-Attention": the draft model's self-attention sees a
+  window of recent tokens (512 for instance), so its own cache stays bounded.
 * [GIST-INTRO] the gist.science page, opening explanation: the target model
   keeps (writes down) the draft proposals it accepts; [GIST-3] its section 3
   "Wichtige Ergebnisse": about 3.5 to 4 tokens are accepted per pass.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * mask = ancestor-or-self ("standard tree attention": a draft token sees its
   own branch, itself included, and no sibling or cousin);
@@ -64,6 +67,7 @@ __all__ = [
     "oracle_attn_split",
     "lse_merge",
     "oracle_prefix_attn",
+    "oracle_window_attn",
     "oracle_commit_kv",
     "oracle_tree_rope",
     "round_bf16",
@@ -329,6 +333,49 @@ def oracle_prefix_attn(q, k_prefix, v_prefix, offsets, scale):
             s = (q[b, :, h, :] @ keys.T) * scale          # [T, L_b]
             o[b, :, h, :], lse[b, h, :] = _masked_softmax_rows(
                 s, np.ones_like(s, dtype=bool), vals)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# Draft sliding-window self-attention over a draft tree ([GIST-2AW])
+# --------------------------------------------------------------------------
+
+def oracle_window_attn(q, k_cache, v_cache, offsets, k_tree, v_tree, parent, scale, window):
+    """Sliding-window self-attention of the draft's tree tokens.
+
+    Positions: key k of sequence b's draft cache (k = 0 .. L_b-1, packed by
+    `offsets` [B+1], the last one the token just before the tree) is at
+    position k; tree node i is at position L_b + depth(i) - 1 on its own
+    branch (the position reading of the tree's rotary embedding).  Row i sees
+    a key iff the key lies on its branch (every cache key does; a tree key iff
+    it is in anc*(i)) and its position p obeys pos(i) - window < p <= pos(i)
+    ([GIST-2AW]: a window of the most recent tokens).  q [B,T,Hq,D];
+    k_cache, v_cache [sum L_b, Hkv, D]; k_tree, v_tree [B,T,Hkv,D];
+    parent [B,T]; window >= 1.  Returns fp64 o [B,T,Hq,D], lse [B,Hq,T].
+    """
+    if int(window) < 1:
+        raise ValueError("window must be at least 1")
+    q = _f64(q)
+    kc, vc, kt, vt = _f64(k_cache), _f64(v_cache), _f64(k_tree), _f64(v_tree)
+    B, T, Hq, Hkv, D, G, off = _shapes(q, kt, offsets)
+    anc = ancestor_matrix(parent)
+    depth = anc.sum(axis=2)
+    o = np.empty((B, T, Hq, D))
+    lse = np.empty((B, Hq, T))
+    for b in range(B):
+        L = int(off[b + 1] - off[b])
+        qpos = L + depth[b] - 1                                    # [T]
+        kpos = np.concatenate([np.arange(L), L + depth[b] - 1])    # [L + T]
+        on_branch = np.ones((T, L + T), dtype=bool)
+        on_branch[:, L:] = anc[b]
+        in_window = (kpos[None, :] <= qpos[:, None]) & (kpos[None, :] > qpos[:, None] - window)
+        visible = on_branch & in_window
+        for g in range(Hkv):
+            keys = np.concatenate([kc[off[b]:off[b + 1], g, :], kt[b, :, g, :]])
+            vals = np.concatenate([vc[off[b]:off[b + 1], g, :], vt[b, :, g, :]])
+            for h in range(g * G, (g + 1) * G):
+                s = (q[b, :, h, :] @ keys.T) * scale        # [T, L_b + T]
+                o[b, :, h, :], lse[b, h, :] = _masked_softmax_rows(s, visible, vals)
     return o, lse
 
 

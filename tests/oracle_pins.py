@@ -413,6 +413,90 @@ def pin_prefix_attn_uniform_keys(orc):
                 assert abs(lse[b, h, i] - (s0 + math.log(L))) < TOL
 
 
+# ------------------------------------------------------------ sliding window
+
+def _window_run(orc, w, window, **over):
+    args = dict(q=w.q, k_cache=w.k_prefix, v_cache=w.v_prefix, offsets=w.offsets.numpy(),
+                k_tree=w.k_tree, v_tree=w.v_tree, parent=w.parent.numpy(), scale=w.scale,
+                window=window)
+    args.update(over)
+    return orc.oracle_window_attn(**args)
+
+
+def pin_window_chain_is_banded_causal(orc):
+    """A chain tree under a window W is causal attention over [cache | tree]
+    restricted to a band: concatenated key j is visible to row i iff
+    L + i - W < j <= L + i (torch CPU fp64 SDPA with that boolean mask)."""
+    T = 7
+    for seed, lens, window in ((41, (9, 3), 4), (42, (12, 0), 9), (43, (2, 5), 30), (44, (6, 6), 1)):
+        w = _case(seed, T=T, trees="chain", prefix_lens=lens)
+        o, lse = _window_run(orc, w, window)
+
+        def band(b, L):
+            i = np.arange(T)[:, None]
+            j = np.arange(L + T)[None, :]
+            return (j <= L + i) & (j > L + i - window)
+        ro, rl = _sdpa_reference(w, band)
+        assert np.max(np.abs(o - ro)) < TOL, (seed, window)
+        assert np.max(np.abs(lse - rl)) < TOL, (seed, window)
+
+
+def pin_window_covering_everything_is_tree_attention(orc):
+    """A window at least as long as cache plus tree hides nothing: plain tree
+    attention (SDPA with the reachability mask), for random trees, a forest
+    and an empty cache."""
+    for seed, trees, lens in ((45, "uniform", (5, 3)), (46, ("bounded", 3, 2), (0, 8)),
+                              (47, "forest", (4, 1))):
+        w = _case(seed, trees=trees, prefix_lens=lens)
+        o, lse = _window_run(orc, w, max(lens) + 6)
+        ro, rl = _sdpa_reference(w, _tree_visible(w))
+        assert np.max(np.abs(o - ro)) < TOL and np.max(np.abs(lse - rl)) < TOL, seed
+
+
+def pin_window_one_is_the_token_itself(orc):
+    """Window 1: every token sees only itself, o = its own value row and
+    lse = its own score."""
+    w = _case(48, trees=("bounded", 3, 2), prefix_lens=(4, 2))
+    o, lse = _window_run(orc, w, 1)
+    G = w.q.shape[2] // w.k_tree.shape[2]
+    for b in range(2):
+        for i in range(6):
+            for h in range(w.q.shape[2]):
+                g = h // G
+                assert np.array_equal(o[b, i, h], w.v_tree[b, i, g].double().numpy())
+                s = w.scale * float(w.q[b, i, h].double() @ w.k_tree[b, i, g].double())
+                assert abs(lse[b, h, i] - s) < TOL
+
+
+def pin_window_uniform_keys(orc):
+    """All keys equal: o is the mean of the values of the W most recent tokens
+    on the row's branch (the cache in order, then the ancestors by depth, the
+    token itself last) and lse = s0 + ln min(W, L + depth(i))."""
+    w = _case(49, B=2, T=6, prefix_lens=(7, 2), trees=("bounded", 4, 2))
+    key = torch.randn(w.k_tree.shape[-1], generator=torch.Generator().manual_seed(2))
+    kp = key.expand_as(w.k_prefix).clone()
+    kt = key.expand_as(w.k_tree).clone()
+    parent = w.parent.numpy()
+    off = w.offsets.numpy()
+    G = w.q.shape[2] // w.k_tree.shape[2]
+    for window in (3, 5, 9):
+        o, lse = _window_run(orc, w, window, k_cache=kp, k_tree=kt)
+        for b in range(2):
+            L = int(off[b + 1] - off[b])
+            reach = _closure(parent[b])
+            for i in range(6):
+                anc = [j for j in range(6) if reach[i, j]]      # topological = by depth
+                for h in range(w.q.shape[2]):
+                    g = h // G
+                    branch = [w.v_prefix[off[b] + j, g].double() for j in range(L)]
+                    branch += [w.v_tree[b, j, g].double() for j in anc]
+                    recent = branch[-window:]
+                    mean = torch.stack(recent).mean(0).numpy()
+                    s0 = w.scale * float(w.q[b, i, h].double() @ key.double())
+                    assert np.max(np.abs(o[b, i, h] - mean)) < TOL, (window, b, i)
+                    assert abs(lse[b, h, i] - (s0 + math.log(min(window, L + len(anc))))) < TOL
+
+
 # ------------------------------------------------------------ KV commit
 
 def pin_commit_hand_example(orc):

@@ -42,6 +42,10 @@ MUTATIONS = {
     "rope_theta_exponent": ("    theta = np.power(float(base), -2.0 * np.arange(half) / D)", "    theta = np.power(float(base), -1.0 * np.arange(half) / D)"),
     "rope_q_only_for_k": ("            for x in (q[b, i], kt[b, i]):", "            for x in (q[b, i],):"),
     "round_ties_away": ("    return np.ldexp(np.rint(m * 256.0) / 256.0, e)", "    return np.ldexp(np.floor(m * 256.0 + 0.5) / 256.0, e)"),
+    "window_off_by_one": ("(kpos[None, :] > qpos[:, None] - window)", "(kpos[None, :] >= qpos[:, None] - window)"),
+    "window_tree_position": ("kpos = np.concatenate([np.arange(L), L + depth[b] - 1])", "kpos = np.concatenate([np.arange(L), L + depth[b]])"),
+    "window_ignores_branch": ("        visible = on_branch & in_window\n", "        visible = in_window\n"),
+    "window_values_from_keys": ("            vals = np.concatenate([vc[off[b]:off[b + 1], g, :], vt[b, :, g, :]])", "            vals = np.concatenate([kc[off[b]:off[b + 1], g, :], vt[b, :, g, :]])"),
     "rows_wrong_head": ("        g = h // G\n        if (b, g) not in cache:", "        g = h % Hkv\n        if (b, g) not in cache:"),
 }
 

@@ -12,7 +12,7 @@ weights are not available.  Shapes follow the attention layers of the named
 model families (Llama-3-8B: 32 query heads / 8 KV heads / head_dim 128;
 QwQ-32B: 40 / 8 / 128); values are N(0, 1).
 
-Recipe (fixed; the design doc repeats it):
+Recipe (fixed):
 
 * config k draws from ``numpy.random.default_rng(1000 + k)``;
 * draw order: the tree(s), then q, k_prefix, v_prefix, k_tree, v_tree, each
