@@ -187,6 +187,78 @@ def row_xattn(args):
     }
 
 
+def row_window(args):
+    """Draft sliding-window self-attention over the QwQ-shaped 64-node tree:
+    window 512 after a 32768-row cache, of which the last 511 rows are visible
+    (ltree_window_attn; split-K partials + merge, the same kernels)."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_config
+
+    W = 512
+    w = make_config(4)
+    dev = "cuda:0"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_prefix.shape[1]
+    e = w.q.element_size()
+    L = sum(w.prefix_lens)
+    q, off = w.q.to(dev), w.offsets.to(dev)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    # rotating copies of the rows the window reads (the last W - 1 of the
+    # cache, as the cache of a sequence of that length) keep every call cold
+    kw, vw = w.k_prefix[L - (W - 1):], w.v_prefix[L - (W - 1):]
+    offw = torch.tensor([0, W - 1], dtype=torch.int32, device=dev)
+    win_bytes = 2 * kw.numel() * e
+    n = max(2, math.ceil(512e6 / win_bytes))
+    kv = [(kw.to(dev), vw.to(dev)) for _ in range(n)]
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty((ta.ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, W),),
+                     dtype=torch.uint8, device=dev)
+
+    def call(s):
+        kc, vc = kv[s % n]
+        return ta.ltree_window_attn(q, kc, vc, offw, kt, vt, mask, o, lse, ws, w.scale, W)
+
+    for s in range(args.warmup):
+        assert call(s) == 0
+    torch.cuda.synchronize()
+    us = time_graph(call, args.steps)
+    # the same result as over the full cache
+    assert ta.ltree_window_attn(q, w.k_prefix.to(dev), w.v_prefix.to(dev), off, kt, vt, mask,
+                                o, lse, ws, w.scale, W) == 0
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    # keys seen by node i: min(W, L + depth(i)), depth = popcount of its mask row
+    depth = np.array([bin(int(x) & (2**64 - 1)).count("1") for x in mask.cpu().view(-1).tolist()])
+    visible = int(np.minimum(W, L + depth).sum())
+    flop = 4 * D * Hq * visible
+    bytes_ = (win_bytes + B * T * Hq * D * e + 2 * B * T * Hkv * D * e + B * T * 8
+              + B * T * Hq * D * 4 + B * Hq * T * 4 + 4 * (B + 1))
+    tflops = flop / (us * 1e-6) / 1e12
+    gbs = bytes_ / (us * 1e-6) / 1e9
+    return {
+        "metric": "draft sliding-window self-attention over the tree, µs/call + TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), 1% of cache rows x8)",
+        "config": {"workload": "draft-window512-qwq32b-gqa40/8-d128-T64", "B": B, "T": T,
+                   "Hq": Hq, "Hkv": Hkv, "D": D, "window": W, "cache_len": L,
+                   "cache": f"cold ({n} rotating copies of the window rows)"},
+        "us_per_call": round(us, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 6), "traffic": None,
+                     "note": f"{bytes_ / 1e6:.2f} MB and {flop / 1e9:.3f} GFLOP per call: "
+                             "launch- and latency-bound"},
+    }
+
+
 def row_commit(args):
     """KV-cache commit of the accepted branch: 4 accepted tokens (about the
     accepted length the pages report) of the QwQ-shaped 64-node tree appended
@@ -285,7 +357,7 @@ def row_rope(args):
     }
 
 
-ROWS = {"xattn": row_xattn, "commit": row_commit, "rope": row_rope}
+ROWS = {"xattn": row_xattn, "window": row_window, "commit": row_commit, "rope": row_rope}
 
 
 def main():

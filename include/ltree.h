@@ -46,6 +46,7 @@ extern "C" {
 
 #define LTREE_VERSION 100 /* 1.0.0 */
 #define LTREE_MAX_TREE 64 /* T limit of this version: one 64-bit mask word per row */
+#define LTREE_MAX_WINDOW (1 << 20) /* largest sliding window of ltree_window_attn */
 
 typedef enum {
   LTREE_OK = 0,
@@ -197,6 +198,47 @@ int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
                       const void* q, const void* k_prefix, const void* v_prefix,
                       const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ltree_window_attn_workspace_bytes -- bytes of workspace ltree_window_attn
+ * needs for these sizes and window (0 when they are invalid).
+ */
+size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window);
+
+/*
+ * ltree_window_attn -- the draft model's sliding-window self-attention over a
+ * draft tree (gist.science page, section 2 "Methodik", part A, item
+ * "Sliding-Window Self-Attention": the draft's self-attention sees a window of
+ * recent tokens, e.g. 512, so its own cache stays bounded).
+ *
+ * Positions: key k of sequence b's draft cache (k = 0 .. L_b - 1; the last is
+ * the token just before the tree) is at position k; tree node i is at
+ * L_b + depth(i) - 1 (depth = nodes on its root path, root = 1), the position
+ * ltree_tree_rope uses.  Node i sees exactly the keys on its own branch (all
+ * cache keys, the tree nodes of anc*(i)) whose position p satisfies
+ * pos(i) - window < p <= pos(i): the last window - depth(i) cache keys and
+ * every ancestor.  Otherwise as ltree_attn (scores, lse, GQA, fp32 outputs).
+ *
+ *   dtype, B, T, Hq, Hkv, D, scale, q, k_tree, v_tree, mask, o, lse, stream
+ *                  as for ltree_attn.
+ *   window         T <= window <= LTREE_MAX_WINDOW.
+ *   k_cache, v_cache  [sum L_b, Hkv, D] packed by cache_offsets [B+1] (as
+ *                  k_prefix/v_prefix of ltree_attn), not NULL; L_b may exceed
+ *                  the window: only the last min(L_b, window - 1) rows of each
+ *                  sequence are read, so a caller may pass the whole history
+ *                  or only a bounded ring of recent rows laid out in order.
+ *   workspace      ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, window)
+ *                  bytes, 256-byte aligned, caller-owned.
+ *
+ * Returns as ltree_attn (LTREE_ERR_INVALID_ARG also for window < T).  A
+ * decreasing cache_offsets table (L_b < 0) turns that sequence's rows into
+ * NaN.  Two kernel launches.
+ */
+int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                      int window, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cache_offsets, const void* k_tree, const void* v_tree,
+                      const uint64_t* mask, float* o, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
 
 /*
  * ltree_commit_kv -- copy the keys and values of the accepted draft tokens from

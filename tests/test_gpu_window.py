@@ -1,0 +1,151 @@
+"""The draft model's sliding-window self-attention over a draft tree on the
+GPU, through the C ABI, against the fp64 oracle.
+
+Small cases cover windows shorter and longer than the cache, an empty cache,
+a window equal to T (the deepest node sees no cache key), windows that are
+not multiples of the 64-key tile, several splits, bf16 and fp32, D = 64 and
+128.  The QwQ-shaped case (window 512 after a 32768-row cache, 64 tree
+tokens, 40/8 heads) is checked on two KV heads' rows."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import BF16_O_TOL, F32_O_TOL, LSE_TOL, say
+from workloads import make_config, make_workload
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    # name: (B, T, Hq, Hkv, D, cache_lens, trees, dtype, window)
+    "w64_chain_eq_T": (1, 64, 8, 2, 128, [1000], "chain", "bf16", 64),
+    "w200_ragged_empty": (3, 40, 8, 2, 128, [700, 0, 150], ("bounded", 6, 4), "bf16", 200),
+    "w512_eight_splits": (1, 64, 10, 2, 128, [3000], ("bounded", 8, 3), "bf16", 512),
+    "w130_d64": (2, 33, 8, 2, 64, [129, 1000], "uniform", "bf16", 130),
+    "w100_fp32_d64": (2, 16, 6, 3, 64, [300, 50], "forest", "f32", 100),
+    "w90_fp32_d128": (2, 24, 4, 2, 128, [500, 20], ("bounded", 6, 4), "f32", 90),
+    "w_covers_all": (2, 32, 8, 2, 128, [100, 37], ("bounded", 6, 4), "bf16", 200),
+    "w64_empty_cache": (1, 20, 4, 2, 128, [0], "uniform", "bf16", 64),
+    # node depth up to 40 against a window 2 keys longer than the cache: rows
+    # near the root see every cache key, deep rows lose the first ones
+    "w_just_past_cache": (1, 40, 8, 2, 128, [300], "chain", "bf16", 302),
+}
+
+
+def _case(name):
+    B, T, Hq, Hkv, D, lens, trees, dtype, window = SMALL[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    w = make_workload(rng, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, prefix_lens=lens, trees=trees,
+                      dtype=dtype, name=name)
+    return w, window
+
+
+def _run(w, window):
+    import tree_attention_amd as ta
+    dev = "cuda"
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    o, lse = ta.window_attn(w.q.to(dev), w.k_prefix.to(dev), w.v_prefix.to(dev),
+                            w.offsets.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask,
+                            w.scale, window)
+    torch.cuda.synchronize()
+    return o.cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def _reference(w, window, heads=None):
+    """Oracle over all KV heads, or over the listed KV heads only (their query
+    heads: a sub-problem of the same definition)."""
+    off = w.offsets.numpy()
+    if heads is None:
+        return oracle.oracle_window_attn(w.q, w.k_prefix, w.v_prefix, off, w.k_tree, w.v_tree,
+                                         w.parent.numpy(), w.scale, window)
+    G = w.q.shape[2] // w.k_tree.shape[2]
+    out = []
+    for g in heads:
+        hs = slice(g * G, (g + 1) * G)
+        out.append((hs, oracle.oracle_window_attn(
+            w.q[:, :, hs], w.k_prefix[:, g:g + 1], w.v_prefix[:, g:g + 1], off,
+            w.k_tree[:, :, g:g + 1], w.v_tree[:, :, g:g + 1], w.parent.numpy(), w.scale,
+            window)))
+    return out
+
+
+def _check(w, o, lse, o_ref, lse_ref):
+    tol = BF16_O_TOL if w.dtype == "bf16" else F32_O_TOL
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    eo = np.max(np.abs(o - o_ref))
+    el = np.max(np.abs(lse - lse_ref))
+    assert eo <= tol, f"o max-abs error {eo:.3e} > {tol}"
+    assert el <= LSE_TOL, f"lse max-abs error {el:.3e} > {LSE_TOL}"
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_parity(name):
+    w, window = _case(name)
+    say("window attn small", name)
+    o, lse = _run(w, window)
+    o_ref, lse_ref = _reference(w, window)
+    _check(w, o, lse, o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("split", [64, 192])
+def test_split_sizes(monkeypatch, split):
+    """Splits of one tile and of three tiles (the first of which is the
+    window's per-row masked head tile)."""
+    monkeypatch.setenv("LTREE_SPLIT_KEYS", str(split))
+    rng = np.random.default_rng(split)
+    w = make_workload(rng, B=2, T=64, Hq=8, Hkv=2, D=128, prefix_lens=[2000, 400],
+                      trees=("bounded", 8, 3), dtype="bf16", outlier_frac=0.01)
+    say("window attn split", split)
+    o, lse = _run(w, 512)
+    o_ref, lse_ref = _reference(w, 512)
+    _check(w, o, lse, o_ref, lse_ref)
+
+
+def test_window_covering_everything_equals_tree_attention():
+    """A window longer than cache plus tree: the same result as ltree_attn."""
+    import tree_attention_amd as ta
+    w, window = _case("w_covers_all")
+    say("window attn vs tree attn")
+    o, lse = _run(w, window)
+    dev = "cuda"
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    o2, lse2 = ta.attn(w.q.to(dev), w.k_prefix.to(dev), w.v_prefix.to(dev), w.offsets.to(dev),
+                       max(w.prefix_lens), w.k_tree.to(dev), w.v_tree.to(dev), mask, w.scale)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(o - o2.cpu().double().numpy())) <= BF16_O_TOL
+    assert np.max(np.abs(lse - lse2.cpu().double().numpy())) <= LSE_TOL
+
+
+def test_qwq_shape_two_kv_heads():
+    """Window 512 over the QwQ-shaped layer's 32768-row cache (only the last
+    511 rows are read), 64 tree tokens, 40/8 heads; KV heads 0 and 5."""
+    w = make_config(4)
+    say("window attn qwq shape")
+    o, lse = _run(w, 512)
+    for hs, (o_ref, lse_ref) in _reference(w, 512, heads=(0, 5)):
+        eo = np.max(np.abs(o[:, :, hs] - o_ref))
+        el = np.max(np.abs(lse[:, hs] - lse_ref))
+        assert eo <= BF16_O_TOL, f"o max-abs error {eo:.3e}"
+        assert el <= LSE_TOL, f"lse max-abs error {el:.3e}"
+
+
+def test_window_shorter_than_tree_is_rejected():
+    """window < T is an argument error, reported before any launch."""
+    import tree_attention_amd as ta
+    rng = np.random.default_rng(3)
+    w = make_workload(rng, B=1, T=16, Hq=4, Hkv=2, D=128, prefix_lens=[40], trees="chain",
+                      dtype="bf16")
+    dev = "cuda"
+    assert ta.ltree_window_attn_workspace_bytes(1, 16, 4, 2, 128, 15) == 0
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    o = torch.empty((1, 16, 4, 128), dtype=torch.float32, device=dev)
+    lse = torch.empty((1, 4, 16), dtype=torch.float32, device=dev)
+    ws = torch.empty((1 << 20,), dtype=torch.uint8, device=dev)
+    say("window attn rejects window < T")
+    st = ta.ltree_window_attn(w.q.to(dev), w.k_prefix.to(dev), w.v_prefix.to(dev),
+                              w.offsets.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask, o,
+                              lse, ws, w.scale, 15)
+    assert st == ta.LTREE_ERR_INVALID_ARG

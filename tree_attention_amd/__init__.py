@@ -29,6 +29,9 @@ from ._binding import (  # noqa: F401
     ltree_status_string,
     ltree_tree_rope,
     ltree_version,
+    ltree_window_attn,
+    ltree_window_attn_workspace_bytes,
     prefix_attn,
+    window_attn,
     workspace_for,
 )

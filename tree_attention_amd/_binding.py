@@ -30,7 +30,8 @@ LTREE_MAX_TREE = 64
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
-            "ltree_attn_merge", "ltree_prefix_attn", "ltree_commit_kv", "ltree_tree_rope")
+            "ltree_attn_merge", "ltree_prefix_attn", "ltree_window_attn_workspace_bytes",
+            "ltree_window_attn", "ltree_commit_kv", "ltree_tree_rope")
 
 
 class LTreeError(RuntimeError):
@@ -55,6 +56,8 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
         "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
+        "ltree_window_attn_workspace_bytes": (S, [I, I, I, I, I, I]),
+        "ltree_window_attn": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, P, P, S, P]),
         "ltree_commit_kv": (I, [I, I, I, I, I, P, P, P, P, P, P, P, I, P, P]),
         "ltree_tree_rope": (I, [I, I, I, I, I, I, P, P, P, P, ctypes.c_double, P]),
     }
@@ -162,7 +165,7 @@ def ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o,
     _dev(workspace, "workspace")
     code = {torch.float32: LTREE_F32, torch.bfloat16: LTREE_BF16}.get(dtype)
     if code is None:
-        raise LTreeError(f"unsupported dtype {dtype}")
+        raise TypeError(f"unsupported dtype {dtype}")
     return _lib.ltree_attn_merge(
         code, B, T, Hq, Hkv, D, _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
@@ -210,6 +213,33 @@ def ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, 
         _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
         _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, window) -> int:
+    return _lib.ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, int(window))
+
+
+def ltree_window_attn(q, k_cache, v_cache, cache_offsets, k_tree, v_tree, mask, o, lse,
+                      workspace, scale, window, stream=None) -> int:
+    """Sliding-window self-attention of the tree tokens: node i sees the keys
+    of its branch within `window` positions (the last window - depth(i) cache
+    rows of its sequence and its ancestors); o, lse as ltree_attn."""
+    B, T, Hq, Hkv, D = _check_attn_inputs(q, k_cache, v_cache, cache_offsets, k_tree,
+                                          v_tree, mask)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    # an empty cache (every L_b = 0) has no storage; the library reads no row
+    # of it then, and takes the tree arrays as the non-null stand-in
+    kc = k_cache if k_cache.numel() else k_tree
+    vc = v_cache if v_cache.numel() else v_tree
+    return _lib.ltree_window_attn(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), int(window), _ptr(q), _ptr(kc),
+        _ptr(vc), _ptr(cache_offsets), _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(o),
+        _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream))
 
 
 def ltree_commit_kv(k_tree, v_tree, accepted, n_accepted, dst_row, k_cache, v_cache,
@@ -304,4 +334,22 @@ def prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, scale, wo
                            workspace, scale, stream)
     if st != LTREE_OK:
         raise LTreeError(st, "ltree_prefix_attn")
+    return o, lse
+
+
+def window_attn(q, k_cache, v_cache, cache_offsets, k_tree, v_tree, mask, scale, window,
+                workspace=None, stream=None):
+    """Allocate o and lse (and the workspace) and run ltree_window_attn."""
+    B, T, Hq, D = q.shape
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = ltree_window_attn_workspace_bytes(B, T, Hq, k_tree.shape[2], D, window)
+        if n == 0:
+            raise LTreeError(LTREE_ERR_INVALID_ARG, "ltree_window_attn_workspace_bytes")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    st = ltree_window_attn(q, k_cache, v_cache, cache_offsets, k_tree, v_tree, mask, o, lse,
+                           workspace, scale, window, stream)
+    if st != LTREE_OK:
+        raise LTreeError(st, "ltree_window_attn")
     return o, lse

@@ -182,18 +182,23 @@ struct Ctx {
   int kstride;          // elements between consecutive keys
   int npk;              // prefix keys of this partial
   bool tree;            // the tree keys follow them
+  bool head;            // sliding window, first split: its first tile is masked per row
+  int hbase;            // then row i sees keys hbase + depth(i) .. of that tile
   int tid, lane, wave, l16, grp;
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
 };
 
 // The per-wave body: NT row tiles (rows rbase + 16*(wave + 8*rt) + l16).
-template <int D, int NT>
+// WIN: the sliding-window variant (the head tile's per-row masking exists
+// only there, so the other variant's registers are not spent on it).
+template <int D, int NT, bool WIN>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
   const int lane = x.lane, l16 = x.l16, grp = x.grp, wave = x.wave, tid = x.tid;
   const int npk = x.npk;
   const bool tree = x.tree;
+  const bool head = WIN && x.head;
   const int T = x.a->T;
 
   // ---- queries of this wave's rows, as the B operand (Q^T) of the QK MFMA
@@ -216,10 +221,16 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       }
     }
     vbits[rt] = 0xffffu;
-    if (tree && ok) {
+    if ((tree || head) && ok) {
       const uint64_t mw = a.mask[static_cast<size_t>(x.b) * a.T + i];
-      vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
-                  (static_cast<uint32_t>((mw >> (32 + 8 * grp)) & 0xffu) << 8);
+      if (tree) {
+        vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
+                    (static_cast<uint32_t>((mw >> (32 + 8 * grp)) & 0xffu) << 8);
+      }
+      if (head) {  // bits 16..21: the row's first visible key of the head tile
+        const int sh = min(max(x.hbase + static_cast<int>(__popcll(mw)), 0), 63);
+        vbits[rt] |= static_cast<uint32_t>(sh) << 16;
+      }
     }
   }
 
@@ -393,9 +404,10 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   };
   f16x8 P[NT];  // probabilities of the current block (the B operand P^T of P.V)
 
-  // S^T = K . Q^T for row tile rt; keys past the end, and tree keys outside
-  // the row's branch, get -inf
-  auto qk = [&](f32x4 (&s)[2], int rt, int H, int valid, bool treeblk, auto MASK_) {
+  // S^T = K . Q^T for row tile rt; keys past the end, tree keys outside the
+  // row's branch and, in the window's head tile, keys before the row's window
+  // get -inf
+  auto qk = [&](f32x4 (&s)[2], int rt, int H, int valid, bool treeblk, bool headblk, auto MASK_) {
 #pragma unroll
     for (int c = 0; c < C::DC; ++c)
 #pragma unroll
@@ -408,6 +420,10 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       // whole loop
       const int nin = min(max(valid - 8 * grp, 0), 8);
       uint32_t bits = (!treeblk ? 0xffu : H ? (vbits[rt] >> 8) : vbits[rt]) & ((1u << nin) - 1u);
+      if (WIN && headblk) {  // this lane's keys are 32H + 8grp + 0..7 of the tile
+        const int sh = static_cast<int>(vbits[rt] >> 16) - (32 * H + 8 * grp);
+        bits &= sh <= 0 ? 0xffu : sh >= 8 ? 0u : (0xffu << sh);
+      }
       asm volatile("" : "+v"(bits));
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
@@ -465,11 +481,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   //
   // Row tile by row tile: the check of row tile rt, then its exponentials
   // with the QK products of row tile rt+1 in flight.
-  auto qk_softmax = [&](auto H_, int valid, bool treeblk, auto MASK_) {
+  auto qk_softmax = [&](auto H_, int valid, bool treeblk, bool headblk, auto MASK_) {
     constexpr int H = decltype(H_)::value;
     f32x4 s[2][2];
     float lm[2];
-    qk(s[0], 0, H, valid, treeblk, MASK_);
+    qk(s[0], 0, H, valid, treeblk, headblk, MASK_);
     lm[0] = lane_max(s[0]);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -478,7 +494,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       probs(s[rt & 1], rt, bsum);
       lsum[rt] += bsum;
       if (rt + 1 < NT) {
-        qk(s[(rt + 1) & 1], rt + 1, H, valid, treeblk, MASK_);
+        qk(s[(rt + 1) & 1], rt + 1, H, valid, treeblk, headblk, MASK_);
         lm[(rt + 1) & 1] = lane_max(s[(rt + 1) & 1]);
         // issue order: the products of row tile rt+1 one at a time between
         // the vector instructions of row tile rt
@@ -535,12 +551,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const int SN = S + 1 < kStages ? S + 1 : 0;
     const bool tt = t == ptiles;
     const int nk = tt ? T : min(kTile, npk - t * kTile);  // real keys of this tile
+    const bool hb = head && t == 0;
     const bool more = t + 1 < ntiles;
     // both blocks always run: a block without real keys (the last tile may
     // hold 32 or fewer) is fully masked, its probabilities are zero
-    qk_softmax(I0{}, min(nk, 32), tt, MASK_);
+    qk_softmax(I0{}, min(nk, 32), tt, hb, MASK_);
     pv(S, I0{}, [&] { kload(S, I1{}); });
-    qk_softmax(I1{}, nk - 32, tt, MASK_);
+    qk_softmax(I1{}, nk - 32, tt, hb, MASK_);
     if (more) {
       wait_own(min(1, ntiles - 2 - t));
       convert(SN);
@@ -566,7 +583,9 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   kload(0, I0{});
   // Full prefix tiles need no mask; the last prefix tile when partial and
   // the tree tile run masked after them, with the stage a run-time value.
-  const int nfull = npk / kTile;
+  // The window variant runs every tile that way (its splits hold a few
+  // tiles, and the first of a sequence is masked per row).
+  const int nfull = WIN ? 0 : npk / kTile;
   int t = 0;
   for (; t + kStages <= nfull; t += kStages) {
     tile(0, t, std::false_type{});
@@ -609,7 +628,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
 }
 
-template <int D, int TPW>
+template <int D, int TPW, bool WIN>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
   __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
@@ -628,17 +647,21 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   const int rb = blockIdx.z % a.row_blocks;
   x.rbase = rb * a.rows_per_wg;
   const int off0 = a.offsets[x.b];
-  const int L = a.offsets[x.b + 1] - off0;
-  if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
-  // slot s: prefix keys [s*chunk, min((s+1)*chunk, L)); the last one (slot 0
-  // when L = 0) also the tree keys
-  const int nparts = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+  int start, n;
+  if (!key_range(a.offsets[x.b + 1] - off0, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
+  // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
+  // (slot 0 when n = 0) also the tree keys
+  const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
   if (x.slot >= nparts) return;
   const int k0 = x.slot * a.chunk;
-  x.npk = max(0, min(a.chunk, L - k0));
+  x.npk = max(0, min(a.chunk, n - k0));
   x.tree = a.has_tree && x.slot == nparts - 1;
+  // window W: node i sees prefix keys from L - W + depth(i) on, i.e. from
+  // key n - W + depth(i) of the range, which lies in its first tile
+  x.head = a.window > 0 && x.slot == 0 && x.npk > 0;
+  x.hbase = n - a.window;
   x.kstride = a.Hkv * D;
-  const size_t row0 = static_cast<size_t>(off0) + k0;
+  const size_t row0 = static_cast<size_t>(off0) + start + k0;
   x.kbase = static_cast<const __bf16*>(a.kp) + (row0 * a.Hkv + x.g) * D;
   x.vbase = static_cast<const __bf16*>(a.vp) + (row0 * a.Hkv + x.g) * D;
   x.ktree = static_cast<const __bf16*>(a.kt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
@@ -656,25 +679,25 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   const int ntw = (tiles - x.wave + kWaves - 1) / kWaves;  // tiles wave, wave+8, ... < tiles
   if constexpr (TPW >= 3) {
     if (ntw >= 3) {
-      run<D, 3>(x);
+      run<D, 3, WIN>(x);
       return;
     }
   }
   if constexpr (TPW >= 2) {
     if (ntw == 2) {
-      run<D, 2>(x);
+      run<D, 2, WIN>(x);
       return;
     }
   }
-  run<D, 1>(x);  // one tile, or none: a wave without rows still stages and syncs
+  run<D, 1, WIN>(x);  // one tile, or none: a wave without rows still stages and syncs
 }
 
-template <int D>
+template <int D, bool WIN>
 hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   switch (tpw) {
-    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1>), grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2>), grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3>), grid, dim3(kThreads), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN>), grid, dim3(kThreads), 0, stream, a); break;
   }
   return hipGetLastError();
 }
@@ -690,7 +713,10 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   a.rows_per_wg = 16 * tiles_per_block;
   a.row_blocks = (p.R + a.rows_per_wg - 1) / a.rows_per_wg;
   const dim3 grid(p.Hkv, p.slots, p.B * a.row_blocks);
-  return p.D == 128 ? launch_d<128>(tpw, grid, a, stream) : launch_d<64>(tpw, grid, a, stream);
+  if (a.window > 0) {
+    return p.D == 128 ? launch_d<128, true>(tpw, grid, a, stream) : launch_d<64, true>(tpw, grid, a, stream);
+  }
+  return p.D == 128 ? launch_d<128, false>(tpw, grid, a, stream) : launch_d<64, false>(tpw, grid, a, stream);
 }
 
 }  // namespace ltree

@@ -43,18 +43,19 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   const int b = blockIdx.z / rblocks;
   const int rb = blockIdx.z % rblocks;
   const int off0 = a.offsets[b];
-  const int L = a.offsets[b + 1] - off0;
-  if (L < 0 || L > a.max_prefix_len) return;  // the merge reports it
-  // slot s: prefix keys [s*chunk, min((s+1)*chunk, L)); the last one (slot 0
-  // when L = 0) also the tree keys
-  const int nparts = L > 0 ? (L + a.chunk - 1) / a.chunk : 1;
+  int start, n;
+  if (!key_range(a.offsets[b + 1] - off0, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
+  // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
+  // (slot 0 when n = 0) also the tree keys
+  const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
   if (slot >= nparts) return;
   const int k0 = slot * a.chunk;
-  const int npk = max(0, min(a.chunk, L - k0));
+  const int npk = max(0, min(a.chunk, n - k0));
   const bool tree = a.has_tree && slot == nparts - 1;
   const size_t kstride = static_cast<size_t>(a.Hkv) * D;
-  const Tin* kp = static_cast<const Tin*>(a.kp) + (static_cast<size_t>(off0 + k0) * a.Hkv + g) * D;
-  const Tin* vp = static_cast<const Tin*>(a.vp) + (static_cast<size_t>(off0 + k0) * a.Hkv + g) * D;
+  const size_t row0 = static_cast<size_t>(off0) + start + k0;
+  const Tin* kp = static_cast<const Tin*>(a.kp) + (row0 * a.Hkv + g) * D;
+  const Tin* vp = static_cast<const Tin*>(a.vp) + (row0 * a.Hkv + g) * D;
   const Tin* kt = static_cast<const Tin*>(a.kt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
   const Tin* vt = static_cast<const Tin*>(a.vt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
 
@@ -68,7 +69,9 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) qv[d] = active ? to_f32(qp[d]) * a.scale_log2 : 0.f;
   }
-  const uint64_t mw = (tree && active) ? a.mask[static_cast<size_t>(b) * a.T + i] : 0ull;
+  const uint64_t mw = ((tree || a.window > 0) && active) ? a.mask[static_cast<size_t>(b) * a.T + i] : 0ull;
+  // window W: this row sees prefix keys from key n - W + depth(i) of the range
+  const int first = a.window > 0 ? n - a.window + static_cast<int>(__popcll(mw)) - k0 : 0;
 
   float m = -INFINITY, l = 0.f;
   float acc[D];
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
     }
     __syncthreads();
     for (int j = 0; j < n; ++j) {
-      if (intree && !((mw >> (t0 + j)) & 1)) continue;
+      if (intree ? !((mw >> (t0 + j)) & 1) : t0 + j < first) continue;
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qv[d], ks[j][d], s);

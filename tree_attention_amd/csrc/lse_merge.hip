@@ -72,7 +72,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     const int32_t* __restrict__ offsets, const void* __restrict__ o_part,
     const float* __restrict__ scale_part, const float* __restrict__ lse_part,
     float* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv, int G, int R,
-    int chunk, int slots, int max_prefix_len) {
+    int chunk, int slots, int max_prefix_len, int window) {
   constexpr int FPL = D / 64;  // features per lane
   const int j = threadIdx.x & 63;
   // rows are ordered (b, h, i) so the lse writes [B, Hq, T] are contiguous;
@@ -88,8 +88,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   float* orow = o + ((static_cast<size_t>(b) * T + i) * Hq + h) * D + j * FPL;
   float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * T + i;
 
-  const int L = offsets[b + 1] - offsets[b];
-  if (L < 0 || L > max_prefix_len) {
+  int start, n;
+  if (!key_range(offsets[b + 1] - offsets[b], window, max_prefix_len, &start, &n)) {
     // The prefix-length table disagrees with max_prefix_len: fail loudly.
     const float nan = __builtin_nanf("");
 #pragma unroll
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   }
   // one partial per prefix split, the last of which also covers the tree
   // keys; one tree-only partial when the prefix is empty
-  const int nparts = L == 0 ? 1 : (L + chunk - 1) / chunk;
+  const int nparts = n == 0 ? 1 : (n + chunk - 1) / chunk;
   const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
   auto part_row = [&](int s) { return (base + s) * R + r; };
 
@@ -167,7 +167,7 @@ void launch_typed(const Plan& p, dim3 grid, const int32_t* offsets, const void* 
                   hipStream_t stream) {
   hipLaunchKernelGGL((lse_merge_kernel<D, SNORM>), grid, dim3(64 * kMergeWaves), 0, stream,
                      offsets, o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G,
-                     p.R, p.chunk, p.slots, p.max_prefix_len);
+                     p.R, p.chunk, p.slots, p.max_prefix_len, p.window);
 }
 
 }  // namespace

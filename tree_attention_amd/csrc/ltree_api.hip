@@ -30,7 +30,9 @@ int device_cu_count() {
   return n;
 }
 
-bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p) {
+bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window) {
+  if (window < 0 || window > LTREE_MAX_WINDOW || (window > 0 && window < T)) return false;
+  if (window > 0) max_prefix_len = window - 1;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) return false;
   if (D != 64 && D != 128) return false;
   if (T > LTREE_MAX_TREE) return false;
@@ -44,15 +46,18 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
   p->G = Hq / Hkv;
   p->R = p->G * T;
   p->max_prefix_len = max_prefix_len;
+  p->window = window;
 
   // Split size: enough prefix splits per KV head that the Hkv heads of one
   // sequence cover every compute unit once; never below 256 keys, so that a
-  // split's partial output stays small next to the keys it reads.
+  // split's partial output stays small next to the keys it reads (a window of
+  // a few hundred keys, whose call is latency-bound, splits down to 64).
   const int cus = device_cu_count();
   const int per_head = (cus + Hkv - 1) / Hkv;
   long chunk = (static_cast<long>(max_prefix_len) + per_head - 1) / per_head;
   chunk = (chunk + 63) / 64 * 64;
-  if (chunk < 256) chunk = 256;
+  const long min_chunk = window > 0 ? 64 : 256;
+  if (chunk < min_chunk) chunk = min_chunk;
   if (const char* env = std::getenv("LTREE_SPLIT_KEYS")) {  // tuning sweeps only
     const long v = std::atol(env);
     if (v >= 64 && v % 64 == 0) chunk = v;
@@ -120,12 +125,14 @@ static int check_sizes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len)
   return LTREE_OK;
 }
 
-// Partials of prefix (+ tree, when has_tree) attention into the workspace.
+// Partials of prefix (+ tree, when has_tree) attention into the workspace;
+// window > 0: sliding-window attention (max_prefix_len is then window - 1).
 static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
                     const void* q, const void* k_prefix, const void* v_prefix,
                     const int32_t* prefix_offsets, int max_prefix_len, bool has_tree,
                     const void* k_tree, const void* v_tree, const uint64_t* mask,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                    void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    int window = 0) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
@@ -143,7 +150,7 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
     return LTREE_ERR_INVALID_ARG;
   }
   Plan p;
-  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p)) return LTREE_ERR_INVALID_ARG;
+  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window)) return LTREE_ERR_INVALID_ARG;
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
 
   ltree::PartialArgs a{};
@@ -171,6 +178,7 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
   a.headroom = 15.f / a.scale_log2;
   a.neg_inv_scale_log2 = -1.f / a.scale_log2;
   a.has_tree = has_tree ? 1 : 0;
+  a.window = window;
 
   hipError_t err;
   if (dtype == LTREE_BF16) {
@@ -190,10 +198,11 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
                   max_prefix_len, true, k_tree, v_tree, mask, workspace, workspace_bytes, stream);
 }
 
-int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
-                     const int32_t* prefix_offsets,
-                     int max_prefix_len, float* o, float* lse, const void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+// Merge of the partials in the workspace into o and lse.
+static int merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
+                 const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
+                 const void* workspace, size_t workspace_bytes, hipStream_t stream,
+                 int window = 0) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
@@ -201,7 +210,7 @@ int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
     return LTREE_ERR_INVALID_ARG;
   }
   Plan p;
-  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p)) return LTREE_ERR_INVALID_ARG;
+  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window)) return LTREE_ERR_INVALID_ARG;
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
   const char* ws = static_cast<const char*>(workspace);
   const hipError_t err = ltree::launch_merge(
@@ -209,6 +218,13 @@ int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
       reinterpret_cast<const float*>(ws + p.scale_part_off),
       reinterpret_cast<const float*>(ws + p.lse_part_off), o, lse, stream);
   return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
+}
+
+int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
+                     const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
+                     const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
+               workspace_bytes, stream);
 }
 
 int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
@@ -236,6 +252,30 @@ int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
   if (st != LTREE_OK) return st;
   return ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse,
                           workspace, workspace_bytes, stream);
+}
+
+size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
+  Plan p;
+  if (window < 1) return 0;
+  return ltree::make_plan(B, T, Hq, Hkv, D, window - 1, &p, window) ? p.bytes : 0;
+}
+
+int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                      int window, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* cache_offsets, const void* k_tree, const void* v_tree,
+                      const uint64_t* mask, float* o, float* lse, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (o == nullptr || lse == nullptr || k_cache == nullptr || v_cache == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (window < 1 || window < T) return LTREE_ERR_INVALID_ARG;
+  if (window > LTREE_MAX_WINDOW) return LTREE_ERR_UNSUPPORTED;
+  int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_cache, v_cache, cache_offsets,
+                    window - 1, true, k_tree, v_tree, mask, workspace, workspace_bytes, stream,
+                    window);
+  if (st != LTREE_OK) return st;
+  return merge(dtype, B, T, Hq, Hkv, D, cache_offsets, window - 1, o, lse, workspace,
+               workspace_bytes, stream, window);
 }
 
 int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void* k_tree,

@@ -15,6 +15,7 @@ namespace ltree {
 struct Plan {
   int B, T, Hq, Hkv, D, G, R;  // R = G*T query rows per (sequence, KV head)
   int max_prefix_len;
+  int window;      // 0, or the sliding window W (then max_prefix_len = W - 1)
   int chunk;       // prefix keys per split (multiple of 64)
   int max_chunks;  // ceil(max_prefix_len / chunk): prefix splits per (b, g)
   int slots;       // max(max_chunks, 1).  Slot s of sequence b holds prefix
@@ -24,7 +25,20 @@ struct Plan {
 };
 
 // Returns false when the sizes are invalid (the caller reports the status).
-bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p);
+// With window > 0 the prefix part of each sequence is at most its last
+// window - 1 keys, and max_prefix_len is taken as window - 1.
+bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window = 0);
+
+// The prefix keys sequence b's partials read, [start, start + n) of its L_b
+// packed rows.  Without a window all of them (false when L_b is out of range:
+// negative or above max_prefix_len); with a window W the last min(L_b, W - 1),
+// the cache keys a token at the tree's first position can see.
+__device__ inline bool key_range(int L, int window, int max_prefix_len, int* start, int* n) {
+  if (L < 0 || (window == 0 && L > max_prefix_len)) return false;
+  *n = window > 0 ? min(L, window - 1) : L;
+  *start = L - *n;
+  return true;
+}
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
@@ -54,6 +68,7 @@ struct PartialArgs {
   int chunk, max_chunks, slots, max_prefix_len;
   int rows_per_wg, row_blocks;
   int has_tree;      // 0: prefix keys only (no tree part; the tree arguments are unused)
+  int window;        // 0, or W: node i sees the last W - depth(i) prefix keys (and its branch)
   float scale_log2;  // scale * log2(e)
   float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
   float neg_inv_scale_log2;  // -1 / scale_log2

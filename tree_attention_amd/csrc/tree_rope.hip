@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kRopeThreads) void tree_rope_kernel(
   constexpr int kHeadsPerPass = kRopeThreads / kHalf;
   const int i = blockIdx.x, b = blockIdx.y;
   const int k = threadIdx.x % kHalf, h0 = threadIdx.x / kHalf;
-  const int depth = __popcll(mask[static_cast<size_t>(b) * T + i]);
+  const int depth = static_cast<int>(__popcll(mask[static_cast<size_t>(b) * T + i]));
   if (depth == 0) return;
   const long p = static_cast<long>(offsets[b + 1]) - offsets[b] + depth - 1;
   const double theta = pow(base, -2.0 * k / D);
