@@ -11,14 +11,19 @@ Infinity Cache, so every step streams its keys from HBM (cold-cache timing).
 Prints one JSON line.  The throughput `value` is algorithmic TFLOP/s of the
 whole call (wall clock over the timed steps, launched as one HIP graph;
 `us_per_call_eager` gives the same steps launched call by call); `roofline`
-rates the dominant
-kernel (the partial-attention kernel) against the bf16 MFMA peak, with its
-duration taken from HIP events recorded on the launch stream around K
-back-to-back launches of it on the same rotating inputs.
-`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
-on the host cores.
+rates the dominant kernel (the partial-attention kernel) against the bf16
+MFMA peak, with its duration taken from HIP events recorded on the launch
+stream around one replay of a graph of K launches of it on the same rotating
+inputs.  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+workload on the host cores.
+
+`--row NAME` measures one of the steps around the verification path instead
+(the draft's cross-attention into the target cache, its sliding-window
+self-attention, the KV-cache commit, the tree rotary embedding) and prints
+that row's own JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 4]
+    python bench.py --row {xattn,window,commit,rope}
 """
 
 from __future__ import annotations
@@ -482,13 +487,18 @@ def main():
     t1 = time.perf_counter()
     ms_per_step_eager = (t1 - t0) * 1000 / K
 
-    # the dominant kernel alone: K launches back to back between two events on
-    # the launch stream (events around every launch would add a cache flush
-    # to each)
+    # the dominant kernel alone: K launches of it captured in a graph and
+    # replayed between two events on the launch stream (events around every
+    # launch would add a cache flush to each; eager launches add the host's
+    # launch gaps)
+    part_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(part_graph):
+        for s in range(K):
+            partials(s)
+    part_graph.replay()
     torch.cuda.synchronize()
     e0.record()
-    for s in range(K):
-        partials(s)
+    part_graph.replay()
     e1.record()
     torch.cuda.synchronize()
     part_us = e0.elapsed_time(e1) * 1000 / K

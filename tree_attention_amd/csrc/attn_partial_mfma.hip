@@ -705,9 +705,21 @@ hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream) {
-  // Row blocking: at most kMaxTPW tiles of 16 rows per wave, 8 waves.
+  // Row blocking: at most kMaxTPW tiles of 16 rows per wave, 8 waves.  Fewer
+  // row tiles per wave (more workgroups, each re-reading its split's keys)
+  // when the (sequence, KV head, split) workgroups alone would leave compute
+  // units idle: the smallest count whose grid still fits the chip once.
   const int tiles = (p.R + 15) / 16;
-  const int row_blocks = (tiles + kWaves * kMaxTPW - 1) / (kWaves * kMaxTPW);
+  const long units = static_cast<long>(p.B) * p.Hkv * p.slots;
+  const int cus = device_cu_count();
+  int max_tpw = kMaxTPW;
+  for (int t = 1; t < kMaxTPW; ++t) {
+    if (units * ((tiles + kWaves * t - 1) / (kWaves * t)) <= cus) {
+      max_tpw = t;
+      break;
+    }
+  }
+  const int row_blocks = (tiles + kWaves * max_tpw - 1) / (kWaves * max_tpw);
   const int tiles_per_block = (tiles + row_blocks - 1) / row_blocks;
   const int tpw = (tiles_per_block + kWaves - 1) / kWaves;
   a.rows_per_wg = 16 * tiles_per_block;
