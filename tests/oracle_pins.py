@@ -35,9 +35,10 @@ def _closure(parent_row: np.ndarray) -> np.ndarray:
     for i, p in enumerate(parent_row):
         if p >= 0:
             A[i, p] = 1
-    R = np.eye(T, dtype=np.int64)
-    for _ in range(max(T, 1)):
-        R = np.minimum(R @ A, 1)
+    # (I + P)^(2^k) by repeated squaring; 2^k >= T covers every path
+    R = A
+    for _ in range(max(T, 2).bit_length()):
+        R = np.minimum(R @ R, 1)
     return R.astype(bool)
 
 
@@ -103,6 +104,29 @@ def pin_mask_random_recursion(orc):
             for i in range(T):
                 parent_row = int(m[p[0, i]]) if p[0, i] >= 0 else 0
                 assert int(m[i]) == parent_row | (1 << i)
+
+
+def pin_mask_multiword(orc):
+    """Trees of more than 64 nodes (several words per row): a chain of 200 has
+    rows 0..i set across words; for random trees row(i) == row(parent(i)) |
+    bit(i) on the whole word vector; bits at j >= T stay zero."""
+    T = 200
+    chain = np.concatenate([[-1], np.arange(T - 1)]).astype(np.int32)[None, :]
+    m = orc.oracle_mask(chain)[0]                       # [T, W]
+    assert m.shape == (T, 4)
+    for i in (0, 63, 64, 127, 150, 199):
+        as_int = sum(int(m[i, w]) << (64 * w) for w in range(4))
+        assert as_int == (1 << (i + 1)) - 1, i
+    rng = np.random.default_rng(8)
+    for T in (65, 130, 256):
+        for kind in ("uniform", ("bounded", 9, 4), "forest"):
+            p = make_tree(rng, T, kind)[None, :]
+            m = orc.oracle_mask(p)[0]
+            rows = [sum(int(m[i, w]) << (64 * w) for w in range(m.shape[1])) for i in range(T)]
+            for i in range(T):
+                parent_row = rows[p[0, i]] if p[0, i] >= 0 else 0
+                assert rows[i] == parent_row | (1 << i)
+                assert rows[i] >> T == 0
 
 
 def pin_check_parent(orc):
@@ -179,6 +203,23 @@ def pin_general_tree_vs_sdpa(orc):
         ro, rl = _sdpa_reference(w, _tree_visible(w))
         assert np.max(np.abs(o - ro)) < TOL, seed
         assert np.max(np.abs(lse - rl)) < TOL, seed
+
+
+def pin_large_tree_vs_sdpa(orc):
+    """A 100-node tree (two mask words per row) and a 70-node chain: oracle ==
+    torch SDPA with the reachability / bottom-right causal mask."""
+    w = _case(14, B=2, T=100, Hq=4, Hkv=2, D=8, prefix_lens=(9, 0), trees=("bounded", 12, 3))
+    o, lse = _run(orc, w)
+    ro, rl = _sdpa_reference(w, _tree_visible(w))
+    assert np.max(np.abs(o - ro)) < TOL and np.max(np.abs(lse - rl)) < TOL
+    T = 70
+    w = _case(15, B=1, T=T, Hq=2, Hkv=1, D=8, prefix_lens=(5,), trees="chain")
+    o, lse = _run(orc, w)
+
+    def causal(b, L):
+        return np.arange(L + T)[None, :] <= L + np.arange(T)[:, None]
+    ro, rl = _sdpa_reference(w, causal)
+    assert np.max(np.abs(o - ro)) < TOL and np.max(np.abs(lse - rl)) < TOL
 
 
 def pin_chain_is_causal(orc):
