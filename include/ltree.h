@@ -45,13 +45,13 @@ extern "C" {
 #endif
 
 #define LTREE_VERSION 100 /* 1.0.0 */
-#define LTREE_MAX_TREE 64 /* T limit of this version: one 64-bit mask word per row */
+#define LTREE_MAX_TREE 256 /* largest tree; a mask row has W = ceil(T / 64) 64-bit words */
 #define LTREE_MAX_WINDOW (1 << 20) /* largest sliding window of ltree_window_attn */
 
 typedef enum {
   LTREE_OK = 0,
   LTREE_ERR_INVALID_ARG = -1, /* null pointer, bad size, Hq % Hkv != 0, scale <= 0, ... */
-  LTREE_ERR_UNSUPPORTED = -2, /* valid but not built: D not 64/128, T > 64, ...        */
+  LTREE_ERR_UNSUPPORTED = -2, /* valid but not built: D not 64/128, T > 256, ...       */
   LTREE_ERR_WORKSPACE = -3,   /* workspace too small or misaligned                     */
   LTREE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed            */
 } ltree_status;
@@ -67,6 +67,9 @@ int ltree_version(void);
 /* Static, human-readable text for a status code (never NULL). */
 const char* ltree_status_string(int status);
 
+/* Words of one mask row for a tree of T nodes: W = ceil(T / 64). */
+#define LTREE_MASK_WORDS(T) (((T) + 63) / 64)
+
 /*
  * ltree_build_mask -- ancestor-or-self bitmask of B speculation trees.
  *
@@ -79,14 +82,15 @@ const char* ltree_status_string(int status);
  *           prefix; otherwise it is an earlier node, 0 <= parent < i.  Several
  *           -1 entries (a forest) are allowed.
  *   B, T    1 <= B, 1 <= T <= LTREE_MAX_TREE.
- *   mask    [B, T] uint64 out.  Bit j of mask[b*T+i] is set iff j == i or j is
+ *   mask    [B, T, W] uint64 out, W = LTREE_MASK_WORDS(T) (1 for T <= 64).
+ *           Bit j % 64 of word j / 64 of row (b, i) is set iff j == i or j is
  *           an ancestor of i.  Bits j >= T are zero.
  *   status  [1] int32 out, or NULL.  0 when every parent entry is valid; else
  *           1 + the smallest flat index b*T+i whose entry is invalid.  All mask
  *           rows of a tree with an invalid entry are written as zero.
  *
  * Returns LTREE_OK, LTREE_ERR_INVALID_ARG (null pointer, B < 1, T < 1),
- * LTREE_ERR_UNSUPPORTED (T > 64) or LTREE_ERR_HIP.  One launch, no workspace.
+ * LTREE_ERR_UNSUPPORTED (T > 256) or LTREE_ERR_HIP.  One launch, no workspace.
  */
 int ltree_build_mask(const int32_t* parent, int B, int T, uint64_t* mask,
                      int32_t* status, hipStream_t stream);
@@ -114,7 +118,7 @@ size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
  *
  *   dtype          LTREE_BF16 or LTREE_F32 for q, k_prefix, v_prefix, k_tree, v_tree.
  *   B, T, Hq, Hkv, D
- *                  batch, tree size (1..64), query heads, KV heads (Hq % Hkv == 0),
+ *                  batch, tree size (1..256), query heads, KV heads (Hq % Hkv == 0),
  *                  head dim (64 or 128).
  *   scale          score scale (usually 1/sqrt(D)); finite and > 0.
  *   q              [B, T, Hq, D] queries of the tree tokens (after RoPE).
@@ -126,9 +130,9 @@ size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
  *                  A sequence whose L_b exceeds it, or whose offsets decrease,
  *                  gets NaN in all its o and lse entries.
  *   k_tree, v_tree [B, T, Hkv, D] keys/values of the tree tokens.
- *   mask           [B, T] uint64 from ltree_build_mask (bit j of row i: node j
- *                  visible to node i).  Row i must have bit i set; a row with no
- *                  visible tree node and L_b = 0 has no defined result.
+ *   mask           [B, T, W] uint64 from ltree_build_mask (bit j of row i: node
+ *                  j visible to node i).  Row i must have bit i set; a row with
+ *                  no visible tree node and L_b = 0 has no defined result.
  *   o              [B, T, Hq, D] fp32 out.
  *   lse            [B, Hq, T] fp32 out, natural logarithm.
  *   workspace      >= ltree_attn_workspace_bytes(...) bytes, 256-byte aligned.
@@ -187,7 +191,7 @@ int ltree_attn_merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
  *
  *   dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix, prefix_offsets,
  *   max_prefix_len, o, lse, workspace, workspace_bytes, stream
- *                  as for ltree_attn; T (1..64) counts the query tokens.  The
+ *                  as for ltree_attn; T (1..256) counts the query tokens.  The
  *                  workspace size is ltree_attn_workspace_bytes(B, T, Hq, Hkv,
  *                  D, max_prefix_len).
  *   A sequence with L_b = 0 has no key: its rows get o = 0 and lse = -inf.
@@ -220,7 +224,7 @@ size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, i
  * every ancestor.  Otherwise as ltree_attn (scores, lse, GQA, fp32 outputs).
  *
  *   dtype, B, T, Hq, Hkv, D, scale, q, k_tree, v_tree, mask, o, lse, stream
- *                  as for ltree_attn.
+ *                  as for ltree_attn, with T <= 64 (one mask word per row).
  *   window         T <= window <= LTREE_MAX_WINDOW.
  *   k_cache, v_cache  [sum L_b, Hkv, D] packed by cache_offsets [B+1] (as
  *                  k_prefix/v_prefix of ltree_attn), not NULL; L_b may exceed
@@ -230,7 +234,8 @@ size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, i
  *   workspace      ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, window)
  *                  bytes, 256-byte aligned, caller-owned.
  *
- * Returns as ltree_attn (LTREE_ERR_INVALID_ARG also for window < T).  A
+ * Returns as ltree_attn (LTREE_ERR_INVALID_ARG also for window < T,
+ * LTREE_ERR_UNSUPPORTED for T > 64).  A
  * decreasing cache_offsets table (L_b < 0) turns that sequence's rows into
  * NaN.  Two kernel launches.
  */
@@ -248,7 +253,7 @@ int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
  * to 4 accepted tokens per pass).
  *
  *   dtype       element type of all four K/V arrays (LTREE_BF16 or LTREE_F32).
- *   B, T, Hkv, D  1 <= T <= 64, D in {64, 128}.
+ *   B, T, Hkv, D  1 <= T <= LTREE_MAX_TREE, D in {64, 128}.
  *   k_tree, v_tree  [B, T, Hkv, D], as given to ltree_attn.
  *   accepted    [B, T] int32: tree node ids of the accepted tokens of sequence
  *               b in cache order (root side first); entries from n_accepted[b]
@@ -278,7 +283,7 @@ int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void*
  * "Trainings-Inferenz-Diskrepanz": positions enter through RoPE and must agree
  * with the target model's; the mlsanity.com page lists RoFormer among the
  * paper's references).  Node i of sequence b takes position
- * p = L_b + depth(i) - 1, depth = popcount(mask row) (root = 1), so a token
+ * p = L_b + depth(i) - 1, depth = popcount of the mask row (root = 1), so a token
  * continues the prefix along its own branch and siblings share a position.
  * For every head and k < D/2, with a = p * rope_base^(-2k/D):
  *   x[k]       <- x[k] cos a - x[k + D/2] sin a
@@ -287,12 +292,12 @@ int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void*
  *
  *   dtype          LTREE_BF16 or LTREE_F32, the type of q and k_tree.
  *   q              [B, T, Hq, D] in/out.   k_tree  [B, T, Hkv, D] in/out.
- *   mask           [B, T] uint64 from ltree_build_mask.  A zero row (a tree
+ *   mask           [B, T, W] uint64 from ltree_build_mask.  A zero row (a tree
  *                  with an invalid parent) leaves that token unrotated.
  *   prefix_offsets [B+1] int32 as for ltree_attn (L_b = o[b+1] - o[b]).
  *   rope_base      > 1, the rotary base of the target model.
  *
- * Returns LTREE_OK, LTREE_ERR_INVALID_ARG, LTREE_ERR_UNSUPPORTED (T > 64,
+ * Returns LTREE_OK, LTREE_ERR_INVALID_ARG, LTREE_ERR_UNSUPPORTED (T > 256,
  * D not 64/128) or LTREE_ERR_HIP.  One kernel launch; run it before ltree_attn.
  */
 int ltree_tree_rope(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, void* q,

@@ -160,7 +160,7 @@ def test_error_paths_with_real_tensors():
     assert ta.ltree_attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 129, d["k_tree"],
                          d["v_tree"], mask, o, lse, ws, -1.0) == ta.LTREE_ERR_INVALID_ARG
     with pytest.raises(ta.LTreeError):
-        ta.build_mask(torch.zeros((2, 65), dtype=torch.int32, device="cuda"))
+        ta.build_mask(torch.zeros((2, 257), dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
 
 

@@ -57,7 +57,7 @@ def test_workspace_sizing():
     assert ta.ltree_attn_workspace_bytes(1, 64, 40, 8, 128, 65536) >= n
     assert ta.ltree_attn_workspace_bytes(1, 64, 40, 8, 128, 0) > 0
     for bad in [(0, 64, 40, 8, 128, 10), (1, 0, 40, 8, 128, 10), (1, 64, 40, 7, 128, 10),
-                (1, 64, 40, 8, 96, 10), (1, 65, 40, 8, 128, 10), (1, 64, 40, 8, 128, -1)]:
+                (1, 64, 40, 8, 96, 10), (1, 257, 40, 8, 128, 10), (1, 64, 40, 8, 128, -1)]:
         assert ta.ltree_attn_workspace_bytes(*bad) == 0, bad
 
 
@@ -69,7 +69,7 @@ def _raw():
 @no_gpu
 @pytest.mark.parametrize("case,expect", [
     (dict(B=0), -1), (dict(T=0), -1), (dict(Hkv=3), -1), (dict(scale=0.0), -1),
-    (dict(scale=float("nan")), -1), (dict(D=96), -2), (dict(T=65), -2), (dict(dtype=7), -1),
+    (dict(scale=float("nan")), -1), (dict(D=96), -2), (dict(T=257), -2), (dict(dtype=7), -1),
     (dict(q=None), -1), (dict(workspace=None), -1), (dict(ws_bytes=16), -3),
     (dict(workspace=0x1010), -3), (dict(q=0x1008), -1), (dict(max_prefix_len=-5), -1),
 ])
@@ -99,4 +99,4 @@ def test_build_mask_argument_errors():
     assert fn(None, 1, 8, 0x1000, None, None) == -1
     assert fn(0x1000, 1, 8, None, None, None) == -1
     assert fn(0x1000, 0, 8, 0x2000, None, None) == -1
-    assert fn(0x1000, 1, 65, 0x2000, None, None) == -2
+    assert fn(0x1000, 1, 257, 0x2000, None, None) == -2

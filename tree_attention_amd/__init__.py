@@ -31,6 +31,8 @@ from ._binding import (  # noqa: F401
     ltree_version,
     ltree_window_attn,
     ltree_window_attn_workspace_bytes,
+    mask_shape,
+    mask_words,
     prefix_attn,
     window_attn,
     workspace_for,

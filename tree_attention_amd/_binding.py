@@ -26,7 +26,7 @@ LTREE_ERR_WORKSPACE = -3
 LTREE_ERR_HIP = -4
 LTREE_F32 = 0
 LTREE_BF16 = 1
-LTREE_MAX_TREE = 64
+LTREE_MAX_TREE = 256
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
@@ -110,14 +110,30 @@ def ltree_status_string(status: int) -> str:
     return _lib.ltree_status_string(int(status)).decode()
 
 
+def mask_words(T) -> int:
+    """64-bit words of one mask row for a tree of T nodes."""
+    return (int(T) + 63) // 64
+
+
+def mask_shape(B, T):
+    """[B, T] for trees of up to 64 nodes, [B, T, W] beyond."""
+    W = mask_words(T)
+    return (B, T) if W == 1 else (B, T, W)
+
+
+def _check_mask(mask, B, T):
+    if tuple(mask.shape) not in ((B, T, mask_words(T)), mask_shape(B, T)):
+        raise ValueError(f"mask must be {list(mask_shape(B, T))}")
+
+
 def ltree_build_mask(parent, mask, status=None, stream=None) -> int:
-    """parent int32 [B, T] -> mask int64 [B, T] (uint64 bits); status int32 [1]."""
+    """parent int32 [B, T] -> mask int64 [B, T] or [B, T, W] (uint64 bits);
+    status int32 [1]."""
     _dev(parent, "parent", torch.int32)
     _dev(mask, "mask", torch.int64)
     _dev(status, "status", torch.int32)
     B, T = parent.shape
-    if mask.shape != (B, T):
-        raise ValueError("mask must be [B, T]")
+    _check_mask(mask, B, T)
     return _lib.ltree_build_mask(_ptr(parent), B, T, _ptr(mask), _ptr(status), _stream(stream))
 
 
@@ -138,8 +154,9 @@ def _check_attn_inputs(q, k_prefix, v_prefix, prefix_offsets, k_tree, v_tree, ma
         raise ValueError("k_tree/v_tree must be [B, T, Hkv, D]")
     if k_prefix.dim() != 3 or k_prefix.shape[1:] != (Hkv, D) or v_prefix.shape != k_prefix.shape:
         raise ValueError("k_prefix/v_prefix must be [sum L, Hkv, D]")
-    if prefix_offsets.shape != (B + 1,) or mask.shape != (B, T):
-        raise ValueError("prefix_offsets must be [B+1] and mask [B, T]")
+    if prefix_offsets.shape != (B + 1,):
+        raise ValueError("prefix_offsets must be [B+1]")
+    _check_mask(mask, B, T)
     return B, T, Hq, Hkv, D
 
 
@@ -275,8 +292,9 @@ def ltree_tree_rope(q, k_tree, mask, prefix_offsets, rope_base, stream=None) -> 
     B, T, Hq, D = q.shape
     if k_tree.dim() != 4 or k_tree.shape[:2] != (B, T) or k_tree.shape[3] != D:
         raise ValueError("k_tree must be [B, T, Hkv, D]")
-    if mask.shape != (B, T) or prefix_offsets.shape != (B + 1,):
-        raise ValueError("mask must be [B, T] and prefix_offsets [B+1]")
+    if prefix_offsets.shape != (B + 1,):
+        raise ValueError("prefix_offsets must be [B+1]")
+    _check_mask(mask, B, T)
     return _lib.ltree_tree_rope(_dtype_code(q), B, T, Hq, k_tree.shape[2], D, _ptr(q),
                                 _ptr(k_tree), _ptr(mask), _ptr(prefix_offsets),
                                 float(rope_base), _stream(stream))
@@ -285,9 +303,10 @@ def ltree_tree_rope(q, k_tree, mask, prefix_offsets, rope_base, stream=None) -> 
 # --------------------------------------------------- allocating conveniences
 
 def build_mask(parent, with_status=True, stream=None):
-    """Allocate and build the mask; returns (mask int64 [B, T], status int32 [1])."""
+    """Allocate and build the mask; returns (mask int64 [B, T] or [B, T, W], status
+    int32 [1])."""
     B, T = parent.shape
-    mask = torch.empty((B, T), dtype=torch.int64, device=parent.device)
+    mask = torch.empty(mask_shape(B, T), dtype=torch.int64, device=parent.device)
     status = torch.empty((1,), dtype=torch.int32, device=parent.device) if with_status else None
     st = ltree_build_mask(parent, mask, status, stream)
     if st != LTREE_OK:

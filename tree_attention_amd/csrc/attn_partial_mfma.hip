@@ -77,6 +77,7 @@ constexpr int kWaves = 8;    // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgroup)
 constexpr int kVtRow = 144;  // bytes per V^T row: 64 fp16 keys + 16 bytes of pitch
+constexpr int kMaskStash = LTREE_MAX_TREE * ((LTREE_MAX_TREE + 63) / 64) * 8;  // LDS bytes, BIGT
 // fourth word of a raw buffer descriptor (32-bit data format; no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
@@ -191,7 +192,10 @@ struct Ctx {
 // The per-wave body: NT row tiles (rows rbase + 16*(wave + 8*rt) + l16).
 // WIN: the sliding-window variant (the head tile's per-row masking exists
 // only there, so the other variant's registers are not spent on it).
-template <int D, int NT, bool WIN>
+// BIGT: trees of more than 64 nodes: ceil(T/64) tree tiles, whose mask bits
+// each row tile reads from a copy of the sequence's mask words in LDS at the
+// start of the tile (W = ceil(T/64) words per row).
+template <int D, int NT, bool WIN, bool BIGT>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
@@ -221,7 +225,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       }
     }
     vbits[rt] = 0xffffu;
-    if ((tree || head) && ok) {
+    if (!BIGT && (tree || head) && ok) {
       const uint64_t mw = a.mask[static_cast<size_t>(x.b) * a.T + i];
       if (tree) {
         vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
@@ -267,9 +271,9 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   const float t8 = a.headroom;             // 15 / c2
   const float nic2 = a.neg_inv_scale_log2;  // -1 / c2
   auto thr = [&](int rt) { return fmaf(nmc[rt], nic2, t8); };
-  // prefix tiles, then one tree tile (T <= 64)
+  // prefix tiles, then the tree tiles (one for T <= 64)
   const int ptiles = (npk + kTile - 1) / kTile;
-  const int ntiles = ptiles + (tree ? 1 : 0);
+  const int ntiles = ptiles + (tree ? (BIGT ? (T + kTile - 1) / kTile : 1) : 0);
   const int kstride = x.kstride;
 
   // ---- per-lane LDS offsets of the MFMA operands.  Stage, block half, sub
@@ -321,9 +325,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     vsoff[i][1] = vsoff[i][0] + kstride * 2;
   }
   auto dma = [&](int S, int t) {
-    const bool tt = t == ptiles;  // the tree tile
-    const int nrows = tt ? T : min(kTile, npk - t * kTile);
-    const size_t toff = tt ? 0 : static_cast<size_t>(t) * kTile * kstride;
+    const bool tt = BIGT ? t >= ptiles : t == ptiles;  // a tree tile
+    const int u = BIGT ? t - ptiles : 0;                // its index among the tree tiles
+    const int nrows = tt ? (BIGT ? min(kTile, T - u * kTile) : T) : min(kTile, npk - t * kTile);
+    const size_t toff = tt ? (BIGT ? static_cast<size_t>(u) * kTile * kstride : 0)
+                           : static_cast<size_t>(t) * kTile * kstride;
     const int bytes = nrows * kstride * 2;
     const auto rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<__bf16*>((tt ? x.ktree : x.kbase) + toff), 0, bytes, kBufferFlags);
@@ -549,8 +555,21 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // S = t % kStages; a compile-time constant in the unrolled main loop.
   auto tile = [&](int S, int t, auto MASK_) {
     const int SN = S + 1 < kStages ? S + 1 : 0;
-    const bool tt = t == ptiles;
-    const int nk = tt ? T : min(kTile, npk - t * kTile);  // real keys of this tile
+    const bool tt = BIGT ? t >= ptiles : t == ptiles;
+    const int u = BIGT ? t - ptiles : 0;
+    const int nk = tt ? (BIGT ? min(kTile, T - u * kTile) : T) : min(kTile, npk - t * kTile);  // real keys of this tile
+    if constexpr (BIGT) {
+      if (tt) {  // this lane's mask bits of tree tile u, from the LDS copy
+        const uint64_t* mst = reinterpret_cast<const uint64_t*>(sm + C::SMEM);
+#pragma unroll
+        for (int rt = 0; rt < NT; ++rt) {
+          const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
+          const uint64_t mw = r < x.rend ? mst[(r / a.G) * a.W + u] : ~0ull;
+          vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
+                      (static_cast<uint32_t>((mw >> (32 + 8 * grp)) & 0xffu) << 8);
+        }
+      }
+    }
     const bool hb = head && t == 0;
     const bool more = t + 1 < ntiles;
     // both blocks always run: a block without real keys (the last tile may
@@ -568,6 +587,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     // keeps the P.V free of branches)
     pv(S, I1{}, [&] { kload(SN, I0{}); });
   };
+  if constexpr (BIGT) {
+    if (tree) {  // the sequence's mask words to LDS, before any tile load is in flight
+      const uint64_t* mrow = a.mask + static_cast<size_t>(x.b) * a.T * a.W;
+      uint64_t* mst = reinterpret_cast<uint64_t*>(sm + C::SMEM);
+      for (int k = tid; k < a.T * a.W; k += kThreads) mst[k] = mrow[k];
+    }
+  }
   // Tile 0 alone first: every workgroup starts at once, and tile 0 arrives
   // sooner when the loads of the next tiles are not competing with it.
   // (no tile at all only for an empty prefix without tree keys: the partial
@@ -628,10 +654,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
 }
 
-template <int D, int TPW, bool WIN>
+template <int D, int TPW, bool WIN, bool BIGT>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
-  __shared__ __attribute__((aligned(1024))) char smem[C::SMEM];
+  static_assert(!(WIN && BIGT), "the window variant takes trees of at most 64 nodes");
+  __shared__ __attribute__((aligned(1024))) char smem[BIGT ? C::SMEM + kMaskStash : C::SMEM];
 
   Ctx x;
   x.a = &a;
@@ -679,25 +706,25 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   const int ntw = (tiles - x.wave + kWaves - 1) / kWaves;  // tiles wave, wave+8, ... < tiles
   if constexpr (TPW >= 3) {
     if (ntw >= 3) {
-      run<D, 3, WIN>(x);
+      run<D, 3, WIN, BIGT>(x);
       return;
     }
   }
   if constexpr (TPW >= 2) {
     if (ntw == 2) {
-      run<D, 2, WIN>(x);
+      run<D, 2, WIN, BIGT>(x);
       return;
     }
   }
-  run<D, 1, WIN>(x);  // one tile, or none: a wave without rows still stages and syncs
+  run<D, 1, WIN, BIGT>(x);  // one tile, or none: a wave without rows still stages and syncs
 }
 
-template <int D, bool WIN>
+template <int D, bool WIN, bool BIGT>
 hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   switch (tpw) {
-    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN>), grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN>), grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN>), grid, dim3(kThreads), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN, BIGT>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN, BIGT>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN, BIGT>), grid, dim3(kThreads), 0, stream, a); break;
   }
   return hipGetLastError();
 }
@@ -725,10 +752,16 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   a.rows_per_wg = 16 * tiles_per_block;
   a.row_blocks = (p.R + a.rows_per_wg - 1) / a.rows_per_wg;
   const dim3 grid(p.Hkv, p.slots, p.B * a.row_blocks);
-  if (a.window > 0) {
-    return p.D == 128 ? launch_d<128, true>(tpw, grid, a, stream) : launch_d<64, true>(tpw, grid, a, stream);
+  if (a.window > 0) {  // T <= 64 (checked by the caller)
+    return p.D == 128 ? launch_d<128, true, false>(tpw, grid, a, stream)
+                      : launch_d<64, true, false>(tpw, grid, a, stream);
   }
-  return p.D == 128 ? launch_d<128, false>(tpw, grid, a, stream) : launch_d<64, false>(tpw, grid, a, stream);
+  if (a.T > 64) {
+    return p.D == 128 ? launch_d<128, false, true>(tpw, grid, a, stream)
+                      : launch_d<64, false, true>(tpw, grid, a, stream);
+  }
+  return p.D == 128 ? launch_d<128, false, false>(tpw, grid, a, stream)
+                    : launch_d<64, false, false>(tpw, grid, a, stream);
 }
 
 }  // namespace ltree

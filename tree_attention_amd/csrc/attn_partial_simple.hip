@@ -69,7 +69,10 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
 #pragma unroll
     for (int d = 0; d < D; ++d) qv[d] = active ? to_f32(qp[d]) * a.scale_log2 : 0.f;
   }
-  const uint64_t mw = ((tree || a.window > 0) && active) ? a.mask[static_cast<size_t>(b) * a.T + i] : 0ull;
+  // this row's mask words (W per row; one when a window is used)
+  const uint64_t* mrow =
+      a.mask != nullptr ? a.mask + (static_cast<size_t>(b) * a.T + i) * a.W : nullptr;
+  const uint64_t mw = (a.window > 0 && active) ? mrow[0] : 0ull;
   // window W: this row sees prefix keys from key n - W + depth(i) of the range
   const int first = a.window > 0 ? n - a.window + static_cast<int>(__popcll(mw)) - k0 : 0;
 
@@ -95,8 +98,10 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
       vs[j][d] = to_f32(vb[key * kstride + d]);
     }
     __syncthreads();
+    // tree keys t0 .. t0 + 31 lie in mask word t0 / 64
+    const uint64_t mwt = (intree && active) ? mrow[t0 / 64] : 0ull;
     for (int j = 0; j < n; ++j) {
-      if (intree ? !((mw >> (t0 + j)) & 1) : t0 + j < first) continue;
+      if (intree ? !((mwt >> ((t0 + j) & 63)) & 1) : t0 + j < first) continue;
       float s = 0.f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = fmaf(qv[d], ks[j][d], s);

@@ -166,6 +166,7 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
   a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.lse_part_off);
   a.B = B;
   a.T = T;
+  a.W = (T + 63) / 64;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.G = p.G;
@@ -269,6 +270,7 @@ int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
     return LTREE_ERR_INVALID_ARG;
   }
   if (window < 1 || window < T) return LTREE_ERR_INVALID_ARG;
+  if (T > 64) return LTREE_ERR_UNSUPPORTED;  // one mask word per row
   if (window > LTREE_MAX_WINDOW) return LTREE_ERR_UNSUPPORTED;
   int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_cache, v_cache, cache_offsets,
                     window - 1, true, k_tree, v_tree, mask, workspace, workspace_bytes, stream,

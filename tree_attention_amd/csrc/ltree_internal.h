@@ -65,6 +65,7 @@ struct PartialArgs {
   float* scale_part;
   float* lse_part;
   int B, T, Hq, Hkv, G, R;
+  int W;             // mask words per row, ceil(T / 64)
   int chunk, max_chunks, slots, max_prefix_len;
   int rows_per_wg, row_blocks;
   int has_tree;      // 0: prefix keys only (no tree part; the tree arguments are unused)

@@ -12,6 +12,10 @@
 // J_i = J_{J_i}, so after k rounds A_i spans 2^k path nodes; six rounds cover
 // any path of a 64-node tree.  Reads of other lanes go through cross-lane
 // shuffles, which see the values of the previous round.
+//
+// Trees of 65..256 nodes (W = ceil(T/64) words per row) take the same pointer
+// jumping with one thread per node of a 256-thread workgroup, A_i held as W
+// words, the previous round's values exchanged through LDS, and eight rounds.
 #include <climits>
 
 #include "ltree_internal.h"
@@ -73,12 +77,68 @@ __global__ __launch_bounds__(1024) void mask_build_kernel(const int32_t* __restr
   }
 }
 
+constexpr int kWideThreads = 256;  // nodes of the largest tree
+constexpr int kWideWords = 4;      // mask words per row of the largest tree
+
+__global__ __launch_bounds__(kWideThreads) void mask_build_wide_kernel(
+    const int32_t* __restrict__ parent, int B, int T, int W, uint64_t* __restrict__ mask,
+    int32_t* __restrict__ status) {
+  __shared__ uint64_t anc_s[kWideThreads][kWideWords];
+  __shared__ int jump_s[kWideThreads];
+  __shared__ int first_bad;
+  const int i = threadIdx.x;
+  if (i == 0) first_bad = INT_MAX;
+  __syncthreads();
+  const bool node = i < T;
+
+  for (int b = 0; b < B; ++b) {
+    const size_t row0 = static_cast<size_t>(b) * T;
+    int p = -1;
+    bool bad = false;
+    if (node) {
+      p = parent[row0 + i];
+      bad = p < -1 || p >= i;
+    }
+    uint64_t anc[kWideWords] = {0ull, 0ull, 0ull, 0ull};
+    if (node) anc[i >> 6] = 1ull << (i & 63);
+    int jump = (node && !bad) ? p : -1;
+#pragma unroll 1
+    for (int round = 0; round < 8; ++round) {
+#pragma unroll
+      for (int w = 0; w < kWideWords; ++w) anc_s[i][w] = anc[w];
+      jump_s[i] = jump;
+      __syncthreads();
+      if (jump >= 0) {  // an earlier node of the same tree
+#pragma unroll
+        for (int w = 0; w < kWideWords; ++w) anc[w] |= anc_s[jump][w];
+        jump = jump_s[jump];
+      }
+      __syncthreads();
+    }
+    const bool tree_bad = __syncthreads_or(bad) != 0;
+    if (bad) atomicMin(&first_bad, static_cast<int>(row0) + i);
+    if (node) {
+      for (int w = 0; w < W; ++w) mask[(row0 + i) * W + w] = tree_bad ? 0ull : anc[w];
+    }
+  }
+
+  __syncthreads();
+  if (i == 0 && status != nullptr) {
+    *status = first_bad == INT_MAX ? 0 : first_bad + 1;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_mask_build(const int32_t* parent, int B, int T, uint64_t* mask,
                              int32_t* status, hipStream_t stream) {
   // One workgroup: the status word needs the minimum over all trees, and the
   // mask is built once per verification step, so B trees per 16 waves is ample.
+  if (T > 64) {
+    hipLaunchKernelGGL(mask_build_wide_kernel, dim3(1), dim3(kWideThreads), 0, stream, parent, B,
+                       T, (T + 63) / 64, mask, status);
+    return hipGetLastError();
+  }
   const int waves = B < 16 ? B : 16;
   hipLaunchKernelGGL(mask_build_kernel, dim3(1), dim3(64 * waves), 0, stream, parent, B, T,
                      mask, status);

@@ -17,7 +17,8 @@
 // place to q [B,T,Hq,D] and k_tree [B,T,Hkv,D].  The angle and the rotation are
 // evaluated in fp64 (positions reach 10^6 radians at theta_0 = 1), then
 // rounded to the storage type.  depth(i) is the popcount of the node's mask
-// row; a zero row (a tree with an invalid parent) is left unrotated.
+// row (its W = ceil(T/64) words); a zero row (a tree with an invalid parent)
+// is left unrotated.
 #include "ltree_internal.h"
 
 namespace ltree {
@@ -61,7 +62,11 @@ __global__ __launch_bounds__(kRopeThreads) void tree_rope_kernel(
   constexpr int kHeadsPerPass = kRopeThreads / kHalf;
   const int i = blockIdx.x, b = blockIdx.y;
   const int k = threadIdx.x % kHalf, h0 = threadIdx.x / kHalf;
-  const int depth = static_cast<int>(__popcll(mask[static_cast<size_t>(b) * T + i]));
+  const int W = (T + 63) / 64;  // mask words per row
+  int depth = 0;
+  for (int w = 0; w < W; ++w) {
+    depth += static_cast<int>(__popcll(mask[(static_cast<size_t>(b) * T + i) * W + w]));
+  }
   if (depth == 0) return;
   const long p = static_cast<long>(offsets[b + 1]) - offsets[b] + depth - 1;
   const double theta = pow(base, -2.0 * k / D);
