@@ -19,11 +19,11 @@ workload on the host cores.
 
 `--row NAME` measures one of the steps around the verification path instead
 (the draft's cross-attention into the target cache, its sliding-window
-self-attention, the KV-cache commit, the tree rotary embedding) and prints
-that row's own JSON line.
+self-attention, verification of a 256-node tree, the KV-cache commit, the
+tree rotary embedding) and prints that row's own JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 4]
-    python bench.py --row {xattn,window,commit,rope}
+    python bench.py --row {xattn,window,bigtree,commit,rope}
 """
 
 from __future__ import annotations
@@ -75,11 +75,12 @@ def algorithmic_counts(w):
     anc = sum(depth_sum(w.parent[b].tolist()) for b in range(B))
     flop_prefix = 4 * D * Hq * T * sum_l
     flop_tree = 4 * D * Hq * anc
+    W = (T + 63) // 64  # mask words per row
     bytes_ = (2 * sum_l * Hkv * D * e + B * T * Hq * D * e + 2 * B * T * Hkv * D * e
-              + B * T * 8 + B * T * Hq * D * 4 + B * Hq * T * 4 + 4 * (B + 1))
+              + B * T * W * 8 + B * T * Hq * D * 4 + B * Hq * T * 4 + 4 * (B + 1))
     # the partial kernel reads q, prefix K/V, tree K/V and the mask
     bytes_partials = (2 * sum_l * Hkv * D * e + B * T * Hq * D * e + 2 * B * T * Hkv * D * e
-                      + B * T * 8)
+                      + B * T * W * 8)
     return flop_prefix + flop_tree, bytes_, bytes_partials
 
 
@@ -264,6 +265,67 @@ def row_window(args):
     }
 
 
+def row_bigtree(args):
+    """Verification of a 256-node tree (depth <= 12, branching <= 3; four mask
+    words per row) on the QwQ-shaped layer: prefix 32768, 40/8 heads, D 128,
+    1% of prefix rows x8 (ltree_attn; the partial kernel's multi-tile tree
+    variant, 1280 query rows per KV head in four row blocks)."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_workload
+
+    rng = np.random.default_rng(2024)
+    w = make_workload(rng, B=1, T=256, Hq=40, Hkv=8, D=128, prefix_lens=[32768],
+                      trees=("bounded", 12, 3), dtype="bf16", outlier_frac=0.01,
+                      name="qwq32b-gqa40/8-d128-L32k-T256")
+    dev = "cuda:0"
+    B, T, Hq, D = w.q.shape
+    L = sum(w.prefix_lens)
+    q, off = w.q.to(dev), w.offsets.to(dev)
+    kt, vt = w.k_tree.to(dev), w.v_tree.to(dev)
+    mask, status = ta.build_mask(w.parent.to(dev))
+    kv_bytes = 2 * w.k_prefix.numel() * w.q.element_size()
+    n = max(2, math.ceil(512e6 / kv_bytes))
+    kp0, vp0 = w.k_prefix.to(dev), w.v_prefix.to(dev)
+    kv = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(n - 1)]
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = ta.workspace_for(q, kt, L)
+
+    def call(s):
+        kp, vp = kv[s % n]
+        return ta.ltree_attn(q, kp, vp, off, L, kt, vt, mask, o, lse, ws, w.scale)
+
+    for s in range(args.warmup):
+        assert call(s) == 0
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    us = time_graph(call, args.steps)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    flop, bytes_, _ = algorithmic_counts(w)
+    tflops = flop / (us * 1e-6) / 1e12
+    return {
+        "metric": "tree-verify attn with a 256-node tree, µs/call + TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), 1% of prefix rows x8)",
+        "config": {"workload": "qwq32b-gqa40/8-d128-L32k-T256", "B": B, "T": T, "Hq": Hq,
+                   "Hkv": 8, "D": D, "prefix_lens": w.prefix_lens,
+                   "cache": f"cold ({n} rotating KV copies)"},
+        "us_per_call": round(us, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "hbm_frac": round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "note": "whole call (partial kernel + merge)"},
+    }
+
+
 def row_commit(args):
     """KV-cache commit of the accepted branch: 4 accepted tokens (about the
     accepted length the pages report) of the QwQ-shaped 64-node tree appended
@@ -362,7 +424,8 @@ def row_rope(args):
     }
 
 
-ROWS = {"xattn": row_xattn, "window": row_window, "commit": row_commit, "rope": row_rope}
+ROWS = {"xattn": row_xattn, "window": row_window, "bigtree": row_bigtree, "commit": row_commit,
+        "rope": row_rope}
 
 
 def main():
