@@ -33,6 +33,7 @@ forms, library routines, invariants and brute force.  No function is
 from .tree_attention_oracle import (  # noqa: F401
     ancestor_matrix,
     check_parent,
+    gather_paged,
     lse_merge,
     oracle_commit_kv,
     oracle_attn,

@@ -68,6 +68,7 @@ __all__ = [
     "lse_merge",
     "oracle_prefix_attn",
     "oracle_window_attn",
+    "gather_paged",
     "oracle_commit_kv",
     "oracle_tree_rope",
     "round_bf16",
@@ -334,6 +335,37 @@ def oracle_prefix_attn(q, k_prefix, v_prefix, offsets, scale):
             o[b, :, h, :], lse[b, h, :] = _masked_softmax_rows(
                 s, np.ones_like(s, dtype=bool), vals)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# Paged prefix cache
+# --------------------------------------------------------------------------
+
+def gather_paged(pages, block_table, seq_lens, page_size):
+    """The packed prefix layout of a paged cache.
+
+    A paged cache keeps the prefix keys (or values) of every sequence in
+    fixed-size pages of a shared pool: pages [num_pages, page_size, Hkv, D].
+    Key j of sequence b lives in page block_table[b, j // page_size] at row
+    j % page_size.  Returns (packed [sum L_b, Hkv, D], offsets [B+1]), the
+    layout `oracle_attn` takes, so paged attention is attention over the
+    gathered keys.  Raises on a page index outside the pool.
+    """
+    pages = np.asarray(pages)
+    bt = np.asarray(block_table, dtype=np.int64)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    B = lens.shape[0]
+    rows = []
+    for b in range(B):
+        for j in range(int(lens[b])):
+            page = int(bt[b, j // page_size])
+            if not 0 <= page < pages.shape[0]:
+                raise ValueError(f"sequence {b}: page {page} outside the pool")
+            rows.append(pages[page, j % page_size])
+    off = np.zeros(B + 1, dtype=np.int64)
+    off[1:] = np.cumsum(lens)
+    packed = np.stack(rows) if rows else np.zeros((0,) + pages.shape[2:], dtype=pages.dtype)
+    return packed, off
 
 
 # --------------------------------------------------------------------------

@@ -454,6 +454,44 @@ def pin_prefix_attn_uniform_keys(orc):
                 assert abs(lse[b, h, i] - (s0 + math.log(L))) < TOL
 
 
+# ------------------------------------------------------------ paged cache
+
+def pin_gather_paged_hand_example(orc):
+    """Two sequences over a pool of three 2-row pages, worked by hand: sequence
+    0 (3 keys) uses pages 2 then 0, sequence 1 (2 keys) page 1."""
+    pool = np.arange(3 * 2 * 1 * 1, dtype=np.float64).reshape(3, 2, 1, 1)  # value = 2*page + row
+    packed, off = orc.gather_paged(pool, np.array([[2, 0], [1, 7]]), np.array([3, 2]), 2)
+    assert off.tolist() == [0, 3, 5]
+    assert packed[:, 0, 0].tolist() == [4.0, 5.0, 0.0, 2.0, 3.0]
+
+
+def pin_gather_paged_contiguous_is_identity(orc):
+    """Pages laid out in order (block_table[b, j] = first page of b + j) give
+    back the packed cache they were cut from, ragged lengths included; a page
+    outside the pool is an error."""
+    rng = np.random.default_rng(61)
+    P, lens = 4, [9, 0, 4]
+    packed = rng.standard_normal((sum(lens), 2, 3))
+    npages = [(n + P - 1) // P for n in lens]
+    pool = np.zeros((sum(npages), P, 2, 3))
+    bt = np.zeros((3, max(npages)), dtype=np.int64)
+    first, row = 0, 0
+    for b, n in enumerate(lens):
+        for j in range(n):
+            pool[first + j // P, j % P] = packed[row + j]
+        bt[b, :npages[b]] = np.arange(first, first + npages[b])
+        first += npages[b]
+        row += n
+    got, off = orc.gather_paged(pool, bt, np.array(lens), P)
+    assert np.array_equal(got, packed) and off.tolist() == [0, 9, 9, 13]
+    try:
+        orc.gather_paged(pool, np.array([[5]]), np.array([1]), P)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a page outside the pool was accepted")
+
+
 # ------------------------------------------------------------ sliding window
 
 def _window_run(orc, w, window, **over):

@@ -46,6 +46,8 @@ MUTATIONS = {
     "window_tree_position": ("kpos = np.concatenate([np.arange(L), L + depth[b] - 1])", "kpos = np.concatenate([np.arange(L), L + depth[b]])"),
     "window_ignores_branch": ("        visible = on_branch & in_window\n", "        visible = in_window\n"),
     "window_values_from_keys": ("            vals = np.concatenate([vc[off[b]:off[b + 1], g, :], vt[b, :, g, :]])", "            vals = np.concatenate([kc[off[b]:off[b + 1], g, :], vt[b, :, g, :]])"),
+    "paged_row_from_page_index": ("            rows.append(pages[page, j % page_size])", "            rows.append(pages[page, j // page_size])"),
+    "paged_wrong_page_slot": ("            page = int(bt[b, j // page_size])", "            page = int(bt[b, j % page_size])"),
     "rows_wrong_head": ("        g = h // G\n        if (b, g) not in cache:", "        g = h % Hkv\n        if (b, g) not in cache:"),
 }
 
