@@ -204,6 +204,46 @@ int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ltree_attn_paged_workspace_bytes -- bytes of workspace ltree_attn_paged needs
+ * for these sizes and page size (0 when they are invalid).
+ */
+size_t ltree_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len,
+                                        int page_size);
+
+/*
+ * ltree_attn_paged -- ltree_attn over a paged prefix cache: the same
+ * computation (gist.science page, section 2 part C: prefix without mask, tree
+ * under the mask, log-sum-exp merge), with the prefix keys and values kept in
+ * fixed-size pages of a shared pool instead of one packed array.  With
+ * k_tree, v_tree and mask all NULL it is the prefix-only attention of
+ * ltree_prefix_attn over the paged cache (the draft's cross-attention into the
+ * target's cache, section 2 part A).
+ *
+ *   k_pages, v_pages  [num_pages, page_size, Hkv, D] page pools (dtype as q).
+ *   num_pages         >= 1, pages in each pool.
+ *   page_size         keys per page, a multiple of 64.
+ *   block_table       [B, max_pages_per_seq] int32: key j of sequence b is row
+ *                     j % page_size of page block_table[b, j / page_size].
+ *                     Entries past a sequence's last page are not read.  A page
+ *                     number outside [0, num_pages) is never dereferenced: the
+ *                     rows of that sequence become NaN.
+ *   seq_lens          [B] int32, L_b = prefix keys of sequence b, 0 <= L_b <=
+ *                     max_prefix_len (a larger one makes its rows NaN).
+ *   max_prefix_len    host int, <= max_pages_per_seq * page_size.
+ *   workspace         ltree_attn_paged_workspace_bytes(B, T, Hq, Hkv, D,
+ *                     max_prefix_len, page_size) bytes, 256-byte aligned.
+ *   everything else   as for ltree_attn (T up to LTREE_MAX_TREE).
+ *
+ * Returns as ltree_attn.  Two kernel launches.
+ */
+int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                     const void* q, const void* k_pages, const void* v_pages, int num_pages,
+                     int page_size, const int32_t* block_table, int max_pages_per_seq,
+                     const int32_t* seq_lens, int max_prefix_len, const void* k_tree,
+                     const void* v_tree, const uint64_t* mask, float* o, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * ltree_window_attn_workspace_bytes -- bytes of workspace ltree_window_attn
  * needs for these sizes and window (0 when they are invalid).
  */

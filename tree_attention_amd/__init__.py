@@ -18,9 +18,12 @@ from ._binding import (  # noqa: F401
     LTREE_OK,
     LTreeError,
     attn,
+    attn_paged,
     build_mask,
     ltree_attn,
     ltree_attn_merge,
+    ltree_attn_paged,
+    ltree_attn_paged_workspace_bytes,
     ltree_attn_partials,
     ltree_attn_workspace_bytes,
     ltree_build_mask,

@@ -30,7 +30,8 @@ LTREE_MAX_TREE = 256
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
-            "ltree_attn_merge", "ltree_prefix_attn", "ltree_window_attn_workspace_bytes",
+            "ltree_attn_merge", "ltree_prefix_attn", "ltree_attn_paged_workspace_bytes",
+            "ltree_attn_paged", "ltree_window_attn_workspace_bytes",
             "ltree_window_attn", "ltree_commit_kv", "ltree_tree_rope")
 
 
@@ -56,6 +57,9 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
         "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
+        "ltree_attn_paged_workspace_bytes": (S, [I, I, I, I, I, I, I]),
+        "ltree_attn_paged": (I, [I, I, I, I, I, I, F, P, P, P, I, I, P, I, P, I, P, P, P, P, P, P,
+                                 S, P]),
         "ltree_window_attn_workspace_bytes": (S, [I, I, I, I, I, I]),
         "ltree_window_attn": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, P, P, S, P]),
         "ltree_commit_kv": (I, [I, I, I, I, I, P, P, P, P, P, P, P, I, P, P]),
@@ -232,6 +236,47 @@ def ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, 
         workspace.numel() * workspace.element_size(), _stream(stream))
 
 
+def ltree_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len, page_size) -> int:
+    return int(_lib.ltree_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, int(max_prefix_len),
+                                                     int(page_size)))
+
+
+def ltree_attn_paged(q, k_pages, v_pages, block_table, seq_lens, max_prefix_len, k_tree, v_tree,
+                     mask, o, lse, workspace, scale, stream=None) -> int:
+    """Tree-verification attention over a paged prefix: k_pages/v_pages
+    [num_pages, page_size, Hkv, D], block_table int32 [B, max_pages_per_seq],
+    seq_lens int32 [B].  k_tree, v_tree and mask all None: prefix only."""
+    dt = q.dtype
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages)):
+        _dev(t, name, dt)
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        _dev(t, name, torch.int32)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    B, T, Hq, D = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[3] != D or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages/v_pages must be [num_pages, page_size, Hkv, D]")
+    num_pages, page_size, Hkv = k_pages.shape[:3]
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    tree = (k_tree, v_tree, mask)
+    if any(t is not None for t in tree):
+        for name, t in (("k_tree", k_tree), ("v_tree", v_tree)):
+            _dev(t, name, dt)
+            if t.shape != (B, T, Hkv, D):
+                raise ValueError(f"{name} must be [B, T, Hkv, D]")
+        _dev(mask, "mask", torch.int64)
+        _check_mask(mask, B, T)
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    return _lib.ltree_attn_paged(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_pages), _ptr(v_pages),
+        num_pages, page_size, _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+        int(max_prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(o), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
 def ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, window) -> int:
     return _lib.ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, int(window))
 
@@ -371,4 +416,23 @@ def window_attn(q, k_cache, v_cache, cache_offsets, k_tree, v_tree, mask, scale,
                            workspace, scale, window, stream)
     if st != LTREE_OK:
         raise LTreeError(st, "ltree_window_attn")
+    return o, lse
+
+
+def attn_paged(q, k_pages, v_pages, block_table, seq_lens, max_prefix_len, k_tree, v_tree, mask,
+               scale, workspace=None, stream=None):
+    """Allocate o and lse (and the workspace) and run ltree_attn_paged."""
+    B, T, Hq, D = q.shape
+    Hkv = k_pages.shape[2]
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        n = ltree_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len, k_pages.shape[1])
+        if n == 0:
+            raise LTreeError(LTREE_ERR_INVALID_ARG, "ltree_attn_paged_workspace_bytes")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    st = ltree_attn_paged(q, k_pages, v_pages, block_table, seq_lens, max_prefix_len, k_tree,
+                          v_tree, mask, o, lse, workspace, scale, stream)
+    if st != LTREE_OK:
+        raise LTreeError(st, "ltree_attn_paged")
     return o, lse

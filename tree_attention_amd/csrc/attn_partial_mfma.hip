@@ -78,6 +78,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgroup)
 constexpr int kVtRow = 144;  // bytes per V^T row: 64 fp16 keys + 16 bytes of pitch
 constexpr int kMaskStash = LTREE_MAX_TREE * ((LTREE_MAX_TREE + 63) / 64) * 8;  // LDS bytes, BIGT
+constexpr int kPageStash = kMaxSplitPages * 4;  // LDS bytes, PAGED: the split's page numbers
 // fourth word of a raw buffer descriptor (32-bit data format; no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
@@ -181,6 +182,7 @@ struct Ctx {
   const __bf16* ktree;  // tree key 0 of this sequence, KV head g
   const __bf16* vtree;
   int kstride;          // elements between consecutive keys
+  int kfirst;           // key index (within the sequence) of this partial's first prefix key
   int npk;              // prefix keys of this partial
   bool tree;            // the tree keys follow them
   bool head;            // sliding window, first split: its first tile is masked per row
@@ -195,7 +197,10 @@ struct Ctx {
 // BIGT: trees of more than 64 nodes: ceil(T/64) tree tiles, whose mask bits
 // each row tile reads from a copy of the sequence's mask words in LDS at the
 // start of the tile (W = ceil(T/64) words per row).
-template <int D, int NT, bool WIN, bool BIGT>
+// PAGED: the prefix keys live in pages of a shared pool; the page numbers of
+// the split are copied to LDS first, and each 64-key tile (never across a
+// page boundary: the page size is a multiple of 64) gets its own base.
+template <int D, int NT, bool WIN, bool BIGT, bool PAGED>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
@@ -324,6 +329,9 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     vsoff[i][0] = ((2 * vm) * kstride + vc * 8) * 2;
     vsoff[i][1] = vsoff[i][0] + kstride * 2;
   }
+  // PAGED: the split's page numbers in LDS (after the mask words, if any)
+  const int32_t* pst = reinterpret_cast<const int32_t*>(sm + C::SMEM + (BIGT ? kMaskStash : 0));
+  const int p0 = PAGED ? x.kfirst / a.page_size : 0;
   auto dma = [&](int S, int t) {
     const bool tt = BIGT ? t >= ptiles : t == ptiles;  // a tree tile
     const int u = BIGT ? t - ptiles : 0;                // its index among the tree tiles
@@ -331,10 +339,19 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const size_t toff = tt ? (BIGT ? static_cast<size_t>(u) * kTile * kstride : 0)
                            : static_cast<size_t>(t) * kTile * kstride;
     const int bytes = nrows * kstride * 2;
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>((tt ? x.ktree : x.kbase) + toff), 0, bytes, kBufferFlags);
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<__bf16*>((tt ? x.vtree : x.vbase) + toff), 0, bytes, kBufferFlags);
+    const __bf16* kb = (tt ? x.ktree : x.kbase) + toff;
+    const __bf16* vb = (tt ? x.vtree : x.vbase) + toff;
+    if constexpr (PAGED) {
+      if (!tt) {  // tile t: keys kfirst + 64t .. of page pst[(kfirst + 64t) / P - p0]
+        const int key = x.kfirst + t * kTile;
+        const int pg = __builtin_amdgcn_readfirstlane(pst[key / a.page_size - p0]);
+        const size_t row = static_cast<size_t>(pg) * a.page_size + key % a.page_size;
+        kb = static_cast<const __bf16*>(a.kp) + row * kstride + x.g * D;
+        vb = static_cast<const __bf16*>(a.vp) + row * kstride + x.g * D;
+      }
+    }
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kb), 0, bytes, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vb), 0, bytes, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < C::KDMA; ++j) {
       char* dst = sm + Cfg<D>::K0 + S * Cfg<D>::BUF + (j * kWaves + wave) * 1024;
@@ -594,6 +611,30 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       for (int k = tid; k < a.T * a.W; k += kThreads) mst[k] = mrow[k];
     }
   }
+  if constexpr (PAGED) {
+    // page numbers of this split's keys; a page outside the pool makes the
+    // partial NaN (the merge then writes NaN rows) and reads nothing
+    const int np = npk > 0 ? (x.kfirst + npk - 1) / a.page_size - p0 + 1 : 0;
+    int32_t* pw = reinterpret_cast<int32_t*>(sm + C::SMEM + (BIGT ? kMaskStash : 0));
+    bool bad = false;
+    for (int k = tid; k < np; k += kThreads) {
+      const int pg = a.block_table[static_cast<size_t>(x.b) * a.max_pages + p0 + k];
+      bad = bad || pg < 0 || pg >= a.num_pages;
+      pw[k] = pg;
+    }
+    if (__syncthreads_or(bad)) {
+      const size_t pb = (static_cast<size_t>(x.b * a.Hkv + x.g) * a.slots + x.slot) * a.R;
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt) {
+        const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
+        if (r < x.rend && grp == 0) {
+          a.lse_part[pb + r] = __builtin_nanf("");
+          a.scale_part[pb + r] = 0.f;
+        }
+      }
+      return;
+    }
+  }
   // Tile 0 alone first: every workgroup starts at once, and tile 0 arrives
   // sooner when the loads of the next tiles are not competing with it.
   // (no tile at all only for an empty prefix without tree keys: the partial
@@ -654,11 +695,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
 }
 
-template <int D, int TPW, bool WIN, bool BIGT>
+template <int D, int TPW, bool WIN, bool BIGT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
   static_assert(!(WIN && BIGT), "the window variant takes trees of at most 64 nodes");
-  __shared__ __attribute__((aligned(1024))) char smem[BIGT ? C::SMEM + kMaskStash : C::SMEM];
+  static_assert(!(WIN && PAGED), "the window variant reads a packed cache");
+  __shared__ __attribute__((aligned(1024)))
+  char smem[C::SMEM + (BIGT ? kMaskStash : 0) + (PAGED ? kPageStash : 0)];
 
   Ctx x;
   x.a = &a;
@@ -673,15 +716,17 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.b = blockIdx.z / a.row_blocks;
   const int rb = blockIdx.z % a.row_blocks;
   x.rbase = rb * a.rows_per_wg;
-  const int off0 = a.offsets[x.b];
+  const int off0 = PAGED ? 0 : a.offsets[x.b];
+  const int L = PAGED ? a.seq_lens[x.b] : a.offsets[x.b + 1] - off0;
   int start, n;
-  if (!key_range(a.offsets[x.b + 1] - off0, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
+  if (!key_range(L, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
   // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
   // (slot 0 when n = 0) also the tree keys
   const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
   if (x.slot >= nparts) return;
   const int k0 = x.slot * a.chunk;
   x.npk = max(0, min(a.chunk, n - k0));
+  x.kfirst = start + k0;
   x.tree = a.has_tree && x.slot == nparts - 1;
   // window W: node i sees prefix keys from L - W + depth(i) on, i.e. from
   // key n - W + depth(i) of the range, which lies in its first tile
@@ -706,27 +751,33 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   const int ntw = (tiles - x.wave + kWaves - 1) / kWaves;  // tiles wave, wave+8, ... < tiles
   if constexpr (TPW >= 3) {
     if (ntw >= 3) {
-      run<D, 3, WIN, BIGT>(x);
+      run<D, 3, WIN, BIGT, PAGED>(x);
       return;
     }
   }
   if constexpr (TPW >= 2) {
     if (ntw == 2) {
-      run<D, 2, WIN, BIGT>(x);
+      run<D, 2, WIN, BIGT, PAGED>(x);
       return;
     }
   }
-  run<D, 1, WIN, BIGT>(x);  // one tile, or none: a wave without rows still stages and syncs
+  run<D, 1, WIN, BIGT, PAGED>(x);  // one tile, or none: a wave without rows still stages and syncs
 }
 
-template <int D, bool WIN, bool BIGT>
+template <int D, bool WIN, bool BIGT, bool PAGED>
 hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   switch (tpw) {
-    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN, BIGT>), grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN, BIGT>), grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN, BIGT>), grid, dim3(kThreads), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
   }
   return hipGetLastError();
+}
+
+template <bool WIN, bool BIGT, bool PAGED>
+hipError_t launch_dd(int D, int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
+  return D == 128 ? launch_d<128, WIN, BIGT, PAGED>(tpw, grid, a, stream)
+                  : launch_d<64, WIN, BIGT, PAGED>(tpw, grid, a, stream);
 }
 
 }  // namespace
@@ -752,16 +803,14 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   a.rows_per_wg = 16 * tiles_per_block;
   a.row_blocks = (p.R + a.rows_per_wg - 1) / a.rows_per_wg;
   const dim3 grid(p.Hkv, p.slots, p.B * a.row_blocks);
-  if (a.window > 0) {  // T <= 64 (checked by the caller)
-    return p.D == 128 ? launch_d<128, true, false>(tpw, grid, a, stream)
-                      : launch_d<64, true, false>(tpw, grid, a, stream);
+  const bool big = a.T > 64;
+  if (a.window > 0) return launch_dd<true, false, false>(p.D, tpw, grid, a, stream);  // T <= 64
+  if (a.block_table != nullptr) {
+    return big ? launch_dd<false, true, true>(p.D, tpw, grid, a, stream)
+               : launch_dd<false, false, true>(p.D, tpw, grid, a, stream);
   }
-  if (a.T > 64) {
-    return p.D == 128 ? launch_d<128, false, true>(tpw, grid, a, stream)
-                      : launch_d<64, false, true>(tpw, grid, a, stream);
-  }
-  return p.D == 128 ? launch_d<128, false, false>(tpw, grid, a, stream)
-                    : launch_d<64, false, false>(tpw, grid, a, stream);
+  return big ? launch_dd<false, true, false>(p.D, tpw, grid, a, stream)
+             : launch_dd<false, false, false>(p.D, tpw, grid, a, stream);
 }
 
 }  // namespace ltree

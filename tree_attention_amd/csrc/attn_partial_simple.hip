@@ -42,9 +42,11 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   const int rblocks = (a.R + kRowsPerWG - 1) / kRowsPerWG;
   const int b = blockIdx.z / rblocks;
   const int rb = blockIdx.z % rblocks;
-  const int off0 = a.offsets[b];
+  const bool paged = a.block_table != nullptr;
+  const int off0 = paged ? 0 : a.offsets[b];
+  const int L = paged ? a.seq_lens[b] : a.offsets[b + 1] - off0;
   int start, n;
-  if (!key_range(a.offsets[b + 1] - off0, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
+  if (!key_range(L, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
   // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
   // (slot 0 when n = 0) also the tree keys
   const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
@@ -61,6 +63,25 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
 
   const int r = rb * kRowsPerWG + tid;
   const bool active = r < a.R;
+  // paged prefix: row of key k (within the sequence) in the page pool; a page
+  // outside the pool makes this partial NaN and nothing is read
+  auto page_row = [&](int k) -> size_t {
+    const int pg = a.block_table[static_cast<size_t>(b) * a.max_pages + k / a.page_size];
+    return static_cast<size_t>(pg) * a.page_size + k % a.page_size;
+  };
+  if (paged) {
+    bool bad = false;
+    const int p0 = (start + k0) / a.page_size;
+    const int np = npk > 0 ? (start + k0 + npk - 1) / a.page_size - p0 + 1 : 0;
+    for (int k = tid; k < np; k += 256) {
+      const int pg = a.block_table[static_cast<size_t>(b) * a.max_pages + p0 + k];
+      bad = bad || pg < 0 || pg >= a.num_pages;
+    }
+    if (__syncthreads_or(bad)) {
+      if (active) a.lse_part[(static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r] = __builtin_nanf("");
+      return;
+    }
+  }
   const int i = active ? r / a.G : 0;
   const int h = g * a.G + (active ? r % a.G : 0);
   float qv[D];
@@ -88,14 +109,20 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
     const bool intree = tt >= ptiles;
     const int t0 = (intree ? tt - ptiles : tt) * kKeysPerTile;
     const int n = min(kKeysPerTile, (intree ? a.T : npk) - t0);
-    const Tin* kb = intree ? kt : kp;
+    const Tin* kb = intree ? kt : kp;  // (a paged prefix tile addresses the pools itself)
     const Tin* vb = intree ? vt : vp;
     __syncthreads();
     for (int e = tid; e < kKeysPerTile * D; e += 256) {
       const int j = e / D, d = e % D;
       const int key = t0 + min(j, n - 1);
-      ks[j][d] = to_f32(kb[key * kstride + d]);
-      vs[j][d] = to_f32(vb[key * kstride + d]);
+      size_t off = key * kstride + d;
+      if (paged && !intree) {
+        off = page_row(start + k0 + key) * kstride + static_cast<size_t>(g) * D + d;
+        kb = static_cast<const Tin*>(a.kp);
+        vb = static_cast<const Tin*>(a.vp);
+      }
+      ks[j][d] = to_f32(kb[off]);
+      vs[j][d] = to_f32(vb[off]);
     }
     __syncthreads();
     // tree keys t0 .. t0 + 31 lie in mask word t0 / 64

@@ -69,7 +69,8 @@ __device__ inline void load_part(const void* o_part, size_t pr, int j, float (&v
 
 template <int D, bool SNORM>
 __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
-    const int32_t* __restrict__ offsets, const void* __restrict__ o_part,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ seq_lens,
+    const void* __restrict__ o_part,
     const float* __restrict__ scale_part, const float* __restrict__ lse_part,
     float* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv, int G, int R,
     int chunk, int slots, int max_prefix_len, int window) {
@@ -89,9 +90,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * T + i;
 
   int start, n;
-  if (!key_range(offsets[b + 1] - offsets[b], window, max_prefix_len, &start, &n)) {
+  const int L = seq_lens != nullptr ? seq_lens[b] : offsets[b + 1] - offsets[b];
+  const float nan = __builtin_nanf("");
+  if (!key_range(L, window, max_prefix_len, &start, &n)) {
     // The prefix-length table disagrees with max_prefix_len: fail loudly.
-    const float nan = __builtin_nanf("");
 #pragma unroll
     for (int f = 0; f < FPL; ++f) orow[f] = nan;
     if (j == 0) *lrow = nan;
@@ -103,10 +105,22 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
   auto part_row = [&](int s) { return (base + s) * R + r; };
 
-  // max and sum of 2^lse over all partials
+  // max and sum of 2^lse over all partials; a NaN partial (a paged split
+  // with a page outside the pool) makes the row NaN
   float mx = -INFINITY;
+  bool bad = false;
   for (int s0 = 0; s0 < nparts; s0 += kBatch) {
-    if (s0 + j < nparts) mx = fmaxf(mx, lse_part[part_row(s0 + j)]);
+    if (s0 + j < nparts) {
+      const float l = lse_part[part_row(s0 + j)];
+      bad = bad || l != l;
+      mx = fmaxf(mx, l);
+    }
+  }
+  if (__any(bad)) {
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) orow[f] = nan;
+    if (j == 0) *lrow = nan;
+    return;
   }
   mx = wave_max(mx);
   if (mx == -INFINITY) {
@@ -162,32 +176,33 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
 }
 
 template <int D, bool SNORM>
-void launch_typed(const Plan& p, dim3 grid, const int32_t* offsets, const void* o_part,
+void launch_typed(const Plan& p, dim3 grid, const int32_t* offsets, const int32_t* seq_lens,
+                  const void* o_part,
                   const float* scale_part, const float* lse_part, float* o, float* lse,
                   hipStream_t stream) {
   hipLaunchKernelGGL((lse_merge_kernel<D, SNORM>), grid, dim3(64 * kMergeWaves), 0, stream,
-                     offsets, o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G,
+                     offsets, seq_lens, o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G,
                      p.R, p.chunk, p.slots, p.max_prefix_len, p.window);
 }
 
 }  // namespace
 
-hipError_t launch_merge(const Plan& p, bool snorm, const int32_t* offsets, const void* o_part,
-                        const float* scale_part, const float* lse_part, float* o, float* lse,
-                        hipStream_t stream) {
+hipError_t launch_merge(const Plan& p, bool snorm, const int32_t* offsets,
+                        const int32_t* seq_lens, const void* o_part, const float* scale_part,
+                        const float* lse_part, float* o, float* lse, hipStream_t stream) {
   const long rows = static_cast<long>(p.B) * p.Hq * p.T;
   const dim3 grid(static_cast<unsigned>((rows + kMergeWaves - 1) / kMergeWaves));
   if (p.D == 128) {
     if (snorm) {
-      launch_typed<128, true>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+      launch_typed<128, true>(p, grid, offsets, seq_lens, o_part, scale_part, lse_part, o, lse, stream);
     } else {
-      launch_typed<128, false>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+      launch_typed<128, false>(p, grid, offsets, seq_lens, o_part, scale_part, lse_part, o, lse, stream);
     }
   } else {
     if (snorm) {
-      launch_typed<64, true>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+      launch_typed<64, true>(p, grid, offsets, seq_lens, o_part, scale_part, lse_part, o, lse, stream);
     } else {
-      launch_typed<64, false>(p, grid, offsets, o_part, scale_part, lse_part, o, lse, stream);
+      launch_typed<64, false>(p, grid, offsets, seq_lens, o_part, scale_part, lse_part, o, lse, stream);
     }
   }
   return hipGetLastError();

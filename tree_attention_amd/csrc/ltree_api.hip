@@ -30,7 +30,9 @@ int device_cu_count() {
   return n;
 }
 
-bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window) {
+bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window,
+               int page_size) {
+  if (page_size < 0 || page_size % 64 != 0) return false;
   if (window < 0 || window > LTREE_MAX_WINDOW || (window > 0 && window < T)) return false;
   if (window > 0) max_prefix_len = window - 1;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) return false;
@@ -65,6 +67,11 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
   // keys of one split are addressed with 32-bit element offsets
   const long cap = ((1L << 31) - 1) / (static_cast<long>(Hkv) * D) / 64 * 64;
   if (chunk > cap) chunk = cap;
+  // a paged split's page numbers fit the kernels' LDS table (a split that
+  // starts inside a page touches one page more than it fills)
+  if (page_size > 0 && chunk > static_cast<long>(kMaxSplitPages - 1) * page_size) {
+    chunk = static_cast<long>(kMaxSplitPages - 1) * page_size;
+  }
   if (chunk < 64) return false;
   p->chunk = static_cast<int>(chunk);
   p->max_chunks = static_cast<int>((max_prefix_len + chunk - 1) / chunk);
@@ -125,19 +132,31 @@ static int check_sizes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len)
   return LTREE_OK;
 }
 
+// A paged prefix: pools of pages and the table that maps each sequence's
+// keys to them (see ltree_attn_paged).
+struct Paging {
+  const int32_t* seq_lens = nullptr;
+  const int32_t* block_table = nullptr;
+  int page_size = 0, max_pages = 0, num_pages = 0;
+};
+
 // Partials of prefix (+ tree, when has_tree) attention into the workspace;
-// window > 0: sliding-window attention (max_prefix_len is then window - 1).
+// window > 0: sliding-window attention (max_prefix_len is then window - 1);
+// pg.block_table != nullptr: a paged prefix (k_prefix/v_prefix are the pools).
 static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
                     const void* q, const void* k_prefix, const void* v_prefix,
                     const int32_t* prefix_offsets, int max_prefix_len, bool has_tree,
                     const void* k_tree, const void* v_tree, const uint64_t* mask,
                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                    int window = 0) {
+                    int window = 0, const Paging& pg = Paging()) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
   if (!(std::isfinite(scale) && scale > 0.f)) return LTREE_ERR_INVALID_ARG;
-  if (q == nullptr || prefix_offsets == nullptr || workspace == nullptr) return LTREE_ERR_INVALID_ARG;
+  if (q == nullptr || workspace == nullptr) return LTREE_ERR_INVALID_ARG;
+  if (pg.block_table == nullptr ? prefix_offsets == nullptr : pg.seq_lens == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
   if (has_tree && (k_tree == nullptr || v_tree == nullptr || mask == nullptr)) {
     return LTREE_ERR_INVALID_ARG;
   }
@@ -150,7 +169,9 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
     return LTREE_ERR_INVALID_ARG;
   }
   Plan p;
-  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window)) return LTREE_ERR_INVALID_ARG;
+  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window, pg.page_size)) {
+    return LTREE_ERR_INVALID_ARG;
+  }
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
 
   ltree::PartialArgs a{};
@@ -180,6 +201,11 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
   a.neg_inv_scale_log2 = -1.f / a.scale_log2;
   a.has_tree = has_tree ? 1 : 0;
   a.window = window;
+  a.seq_lens = pg.seq_lens;
+  a.block_table = pg.block_table;
+  a.page_size = pg.page_size;
+  a.max_pages = pg.max_pages;
+  a.num_pages = pg.num_pages;
 
   hipError_t err;
   if (dtype == LTREE_BF16) {
@@ -203,19 +229,22 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
 static int merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
                  const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
                  const void* workspace, size_t workspace_bytes, hipStream_t stream,
-                 int window = 0) {
+                 int window = 0, const Paging& pg = Paging()) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
-  if (prefix_offsets == nullptr || o == nullptr || lse == nullptr || workspace == nullptr) {
+  if ((pg.seq_lens == nullptr && prefix_offsets == nullptr) || o == nullptr || lse == nullptr ||
+      workspace == nullptr) {
     return LTREE_ERR_INVALID_ARG;
   }
   Plan p;
-  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window)) return LTREE_ERR_INVALID_ARG;
+  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window, pg.page_size)) {
+    return LTREE_ERR_INVALID_ARG;
+  }
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
   const char* ws = static_cast<const char*>(workspace);
   const hipError_t err = ltree::launch_merge(
-      p, dtype == LTREE_BF16, prefix_offsets, ws + p.o_part_off,
+      p, dtype == LTREE_BF16, prefix_offsets, pg.seq_lens, ws + p.o_part_off,
       reinterpret_cast<const float*>(ws + p.scale_part_off),
       reinterpret_cast<const float*>(ws + p.lse_part_off), o, lse, stream);
   return err == hipSuccess ? LTREE_OK : LTREE_ERR_HIP;
@@ -278,6 +307,44 @@ int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
   if (st != LTREE_OK) return st;
   return merge(dtype, B, T, Hq, Hkv, D, cache_offsets, window - 1, o, lse, workspace,
                workspace_bytes, stream, window);
+}
+
+size_t ltree_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len,
+                                        int page_size) {
+  Plan p;
+  if (page_size < 64) return 0;
+  return ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, 0, page_size) ? p.bytes : 0;
+}
+
+int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                     const void* q, const void* k_pages, const void* v_pages, int num_pages,
+                     int page_size, const int32_t* block_table, int max_pages_per_seq,
+                     const int32_t* seq_lens, int max_prefix_len, const void* k_tree,
+                     const void* v_tree, const uint64_t* mask, float* o, float* lse,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (o == nullptr || lse == nullptr || k_pages == nullptr || v_pages == nullptr ||
+      block_table == nullptr || seq_lens == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (page_size < 64 || page_size % 64 != 0 || num_pages < 1 || max_pages_per_seq < 1 ||
+      max_prefix_len < 0 ||
+      static_cast<long>(max_prefix_len) > static_cast<long>(max_pages_per_seq) * page_size) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  // page rows are addressed with 64-bit offsets; a page's rows with 32-bit ones
+  if (static_cast<long>(page_size) * Hkv * D > (1L << 30)) return LTREE_ERR_UNSUPPORTED;
+  const bool has_tree = k_tree != nullptr || v_tree != nullptr || mask != nullptr;
+  Paging pg;
+  pg.seq_lens = seq_lens;
+  pg.block_table = block_table;
+  pg.page_size = page_size;
+  pg.max_pages = max_pages_per_seq;
+  pg.num_pages = num_pages;
+  int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_pages, v_pages, nullptr, max_prefix_len,
+                    has_tree, k_tree, v_tree, mask, workspace, workspace_bytes, stream, 0, pg);
+  if (st != LTREE_OK) return st;
+  return merge(dtype, B, T, Hq, Hkv, D, nullptr, max_prefix_len, o, lse, workspace,
+               workspace_bytes, stream, 0, pg);
 }
 
 int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void* k_tree,

@@ -24,10 +24,17 @@ struct Plan {
   size_t o_part_off, scale_part_off, lse_part_off, bytes;  // workspace layout
 };
 
+// Page numbers of one split that the paged kernels hold in LDS: a split
+// covers at most (kMaxSplitPages - 1) * page_size keys.
+constexpr int kMaxSplitPages = 448;
+
 // Returns false when the sizes are invalid (the caller reports the status).
 // With window > 0 the prefix part of each sequence is at most its last
 // window - 1 keys, and max_prefix_len is taken as window - 1.
-bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window = 0);
+// page_size > 0: a paged prefix; splits are capped so their pages fit the
+// kernels' LDS table.
+bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window = 0,
+               int page_size = 0);
 
 // The prefix keys sequence b's partials read, [start, start + n) of its L_b
 // packed rows.  Without a window all of them (false when L_b is out of range:
@@ -70,6 +77,12 @@ struct PartialArgs {
   int rows_per_wg, row_blocks;
   int has_tree;      // 0: prefix keys only (no tree part; the tree arguments are unused)
   int window;        // 0, or W: node i sees the last W - depth(i) prefix keys (and its branch)
+  // paged prefix (block_table != nullptr): kp/vp are page pools
+  // [num_pages][page_size][Hkv][D]; key j of sequence b is row j % page_size
+  // of page block_table[b * max_pages + j / page_size]; L_b = seq_lens[b]
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+  int page_size, max_pages, num_pages;
   float scale_log2;  // scale * log2(e)
   float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
   float neg_inv_scale_log2;  // -1 / scale_log2
@@ -95,8 +108,9 @@ hipError_t launch_tree_rope(bool bf16, void* q, void* k_tree, const uint64_t* ma
                             double base, hipStream_t stream);
 
 // snorm: o_part holds int16 snorm values with per-row scales (bf16 path).
-hipError_t launch_merge(const Plan& plan, bool snorm, const int32_t* offsets, const void* o_part,
-                        const float* scale_part, const float* lse_part, float* o, float* lse,
-                        hipStream_t stream);
+// seq_lens != nullptr: L_b = seq_lens[b] (paged prefix), else offsets[b+1] - offsets[b].
+hipError_t launch_merge(const Plan& plan, bool snorm, const int32_t* offsets,
+                        const int32_t* seq_lens, const void* o_part, const float* scale_part,
+                        const float* lse_part, float* o, float* lse, hipStream_t stream);
 
 }  // namespace ltree
