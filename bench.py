@@ -19,11 +19,12 @@ workload on the host cores.
 
 `--row NAME` measures one of the steps around the verification path instead
 (the draft's cross-attention into the target cache, its sliding-window
-self-attention, verification of a 256-node tree, the KV-cache commit, the
-tree rotary embedding) and prints that row's own JSON line.
+self-attention, verification of a 256-node tree, verification over a paged
+cache, the KV-cache commit, the tree rotary embedding) and prints that row's
+own JSON line.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 4]
-    python bench.py --row {xattn,window,bigtree,commit,rope}
+    python bench.py --row {xattn,window,bigtree,paged,commit,rope}
 """
 
 from __future__ import annotations
@@ -326,6 +327,74 @@ def row_bigtree(args):
     }
 
 
+def row_paged(args):
+    """Verification over a paged prefix cache: the QwQ-shaped layer (prefix
+    32768, 64-node tree, 40/8 heads, D 128, 1% of prefix rows x8) with its
+    prefix cut into 256-key pages placed in shuffled order in the page pool
+    (ltree_attn_paged)."""
+    import math
+
+    import numpy as np
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_config
+
+    P = 256
+    w = make_config(4)
+    dev = "cuda:0"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_prefix.shape[1]
+    L = sum(w.prefix_lens)
+    npages = L // P
+    perm = torch.from_numpy(np.random.default_rng(31).permutation(npages)).long()
+    # page perm[j] holds keys j*P .. j*P + P - 1
+    kpool = torch.empty((npages, P, Hkv, D), dtype=w.k_prefix.dtype)
+    vpool = torch.empty_like(kpool)
+    kpool[perm] = w.k_prefix.view(npages, P, Hkv, D)
+    vpool[perm] = w.v_prefix.view(npages, P, Hkv, D)
+    bt = perm.to(torch.int32).view(1, npages).to(dev)
+    lens = torch.tensor([L], dtype=torch.int32, device=dev)
+    kv_bytes = 2 * w.k_prefix.numel() * w.q.element_size()
+    n = max(2, math.ceil(512e6 / kv_bytes))
+    pools = [(kpool.to(dev), vpool.to(dev)) for _ in range(n)]
+    q, kt, vt = w.q.to(dev), w.k_tree.to(dev), w.v_tree.to(dev)
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty((ta.ltree_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, L, P),),
+                     dtype=torch.uint8, device=dev)
+
+    def call(s):
+        kp, vp = pools[s % n]
+        return ta.ltree_attn_paged(q, kp, vp, bt, lens, L, kt, vt, mask, o, lse, ws, w.scale)
+
+    for s in range(args.warmup):
+        assert call(s) == 0
+    torch.cuda.synchronize()
+    us = time_graph(call, args.steps)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    flop, bytes_, _ = algorithmic_counts(w)
+    bytes_ += B * npages * 4 + B * 4          # block table and lengths
+    tflops = flop / (us * 1e-6) / 1e12
+    return {
+        "metric": "tree-verify attn over a paged KV cache, µs/call + TFLOP/s",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), 1% of prefix rows x8)",
+        "config": {"workload": "qwq32b-gqa40/8-d128-L32k-T64-paged256", "B": B, "T": T,
+                   "Hq": Hq, "Hkv": Hkv, "D": D, "prefix_lens": w.prefix_lens, "page_size": P,
+                   "cache": f"cold ({n} rotating page pools)"},
+        "us_per_call": round(us, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None,
+                     "hbm_frac": round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "note": "whole call (partial kernel + merge)"},
+    }
+
+
 def row_commit(args):
     """KV-cache commit of the accepted branch: 4 accepted tokens (about the
     accepted length the pages report) of the QwQ-shaped 64-node tree appended
@@ -424,8 +493,8 @@ def row_rope(args):
     }
 
 
-ROWS = {"xattn": row_xattn, "window": row_window, "bigtree": row_bigtree, "commit": row_commit,
-        "rope": row_rope}
+ROWS = {"xattn": row_xattn, "window": row_window, "bigtree": row_bigtree, "paged": row_paged,
+        "commit": row_commit, "rope": row_rope}
 
 
 def main():
