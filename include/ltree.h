@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LTREE_VERSION 100 /* 1.0.0 */
+#define LTREE_VERSION 110 /* 1.1.0: paged caches, trees of up to 256 nodes, draft-side calls */
 #define LTREE_MAX_TREE 256 /* largest tree; a mask row has W = ceil(T / 64) 64-bit words */
 #define LTREE_MAX_WINDOW (1 << 20) /* largest sliding window of ltree_window_attn */
 

@@ -29,7 +29,9 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("ltree_build_mask", "ltree_attn", "ltree_attn_workspace_bytes",
               "ltree_attn_partials", "ltree_attn_merge", "ltree_status_string",
-              "ltree_version"):
+              "ltree_version", "ltree_prefix_attn", "ltree_window_attn",
+              "ltree_window_attn_workspace_bytes", "ltree_attn_paged",
+              "ltree_attn_paged_workspace_bytes", "ltree_tree_rope", "ltree_commit_kv"):
         assert n in names
 
 
@@ -43,7 +45,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     import tree_attention_amd as ta
-    assert ta.ltree_version() == 100
+    assert ta.ltree_version() == 110
     assert ta.ltree_status_string(0) == "ok"
     assert "workspace" in ta.ltree_status_string(ta.LTREE_ERR_WORKSPACE)
     assert ta.ltree_status_string(12345) == "unknown status"
