@@ -331,7 +331,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
   // PAGED: the split's page numbers in LDS (after the mask words, if any)
   const int32_t* pst = reinterpret_cast<const int32_t*>(sm + C::SMEM + (BIGT ? kMaskStash : 0));
-  const int p0 = PAGED ? x.kfirst / a.page_size : 0;
+  const int p0 = PAGED ? (a.page_shift >= 0 ? x.kfirst >> a.page_shift : x.kfirst / a.page_size) : 0;
   auto dma = [&](int S, int t) {
     const bool tt = BIGT ? t >= ptiles : t == ptiles;  // a tree tile
     const int u = BIGT ? t - ptiles : 0;                // its index among the tree tiles
@@ -344,8 +344,10 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     if constexpr (PAGED) {
       if (!tt) {  // tile t: keys kfirst + 64t .. of page pst[(kfirst + 64t) / P - p0]
         const int key = x.kfirst + t * kTile;
-        const int pg = __builtin_amdgcn_readfirstlane(pst[key / a.page_size - p0]);
-        const size_t row = static_cast<size_t>(pg) * a.page_size + key % a.page_size;
+        const int slot = a.page_shift >= 0 ? key >> a.page_shift : key / a.page_size;
+        const int in_page = a.page_shift >= 0 ? key & (a.page_size - 1) : key % a.page_size;
+        const int pg = __builtin_amdgcn_readfirstlane(pst[slot - p0]);
+        const size_t row = static_cast<size_t>(pg) * a.page_size + in_page;
         kb = static_cast<const __bf16*>(a.kp) + row * kstride + x.g * D;
         vb = static_cast<const __bf16*>(a.vp) + row * kstride + x.g * D;
       }

@@ -206,6 +206,10 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
   a.page_size = pg.page_size;
   a.max_pages = pg.max_pages;
   a.num_pages = pg.num_pages;
+  a.page_shift = -1;
+  if (pg.page_size > 0 && (pg.page_size & (pg.page_size - 1)) == 0) {
+    a.page_shift = __builtin_ctz(static_cast<unsigned>(pg.page_size));
+  }
 
   hipError_t err;
   if (dtype == LTREE_BF16) {

@@ -83,6 +83,7 @@ struct PartialArgs {
   const int32_t* seq_lens;
   const int32_t* block_table;
   int page_size, max_pages, num_pages;
+  int page_shift;    // log2(page_size) when it is a power of two, else -1
   float scale_log2;  // scale * log2(e)
   float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
   float neg_inv_scale_log2;  // -1 / scale_log2
