@@ -8,10 +8,13 @@
 // rows over one prefix split, or over the tree tokens, normalised by its own
 // sum, plus log2 of that sum.  The log-sum-exp merge joins the partials.
 //
-// Grid (Hkv, slots, B * row blocks); one query row per thread; keys are staged
-// 32 at a time in LDS as fp32 and read by every thread (broadcast reads).  The
-// last prefix split of a sequence (slot 0 when its prefix is empty) continues
-// over the tree keys.
+// Grid (Hkv, slots, B * row blocks); `tpr` threads per query row (a power of
+// two up to 32, more when there are few rows, so that small problems still
+// occupy the workgroup): each takes every tpr-th key with its own online
+// softmax state, and the tpr states are joined by wavefront shuffles at the
+// end.  Keys are staged 32 at a time in LDS as fp32 and read by every thread
+// (broadcast reads).  The last prefix split of a sequence (slot 0 when its
+// prefix is empty) continues over the tree keys.
 #include "ltree_internal.h"
 
 namespace ltree {
@@ -29,17 +32,20 @@ __device__ inline float to_f32<__bf16>(__bf16 x) {
 }
 
 constexpr int kKeysPerTile = 32;
-constexpr int kRowsPerWG = 256;
+constexpr int kThreadsWG = 256;
 
 template <typename Tin, int D>
-__global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
+__global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs a) {
   __shared__ float ks[kKeysPerTile][D + 1];
   __shared__ float vs[kKeysPerTile][D + 1];
 
   const int tid = threadIdx.x;
   const int g = blockIdx.x;
   const int slot = blockIdx.y;
-  const int rblocks = (a.R + kRowsPerWG - 1) / kRowsPerWG;
+  const int tpr = a.simple_tpr;                  // threads per row
+  const int rows_per_wg = kThreadsWG / tpr;
+  const int sub = tid % tpr;                     // this thread's share of the keys
+  const int rblocks = (a.R + rows_per_wg - 1) / rows_per_wg;
   const int b = blockIdx.z / rblocks;
   const int rb = blockIdx.z % rblocks;
   const bool paged = a.block_table != nullptr;
@@ -61,7 +67,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
   const Tin* kt = static_cast<const Tin*>(a.kt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
   const Tin* vt = static_cast<const Tin*>(a.vt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
 
-  const int r = rb * kRowsPerWG + tid;
+  const int r = rb * rows_per_wg + tid / tpr;
   const bool active = r < a.R;
   // paged prefix: row of key k (within the sequence) in the page pool; a page
   // outside the pool makes this partial NaN and nothing is read
@@ -73,12 +79,12 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
     bool bad = false;
     const int p0 = (start + k0) / a.page_size;
     const int np = npk > 0 ? (start + k0 + npk - 1) / a.page_size - p0 + 1 : 0;
-    for (int k = tid; k < np; k += 256) {
+    for (int k = tid; k < np; k += kThreadsWG) {
       const int pg = a.block_table[static_cast<size_t>(b) * a.max_pages + p0 + k];
       bad = bad || pg < 0 || pg >= a.num_pages;
     }
     if (__syncthreads_or(bad)) {
-      if (active) a.lse_part[(static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r] = __builtin_nanf("");
+      if (active && sub == 0) a.lse_part[(static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r] = __builtin_nanf("");
       return;
     }
   }
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
     const Tin* kb = intree ? kt : kp;  // (a paged prefix tile addresses the pools itself)
     const Tin* vb = intree ? vt : vp;
     __syncthreads();
-    for (int e = tid; e < kKeysPerTile * D; e += 256) {
+    for (int e = tid; e < kKeysPerTile * D; e += kThreadsWG) {
       const int j = e / D, d = e % D;
       const int key = t0 + min(j, n - 1);
       size_t off = key * kstride + d;
@@ -127,7 +133,7 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
     __syncthreads();
     // tree keys t0 .. t0 + 31 lie in mask word t0 / 64
     const uint64_t mwt = (intree && active) ? mrow[t0 / 64] : 0ull;
-    for (int j = 0; j < n; ++j) {
+    for (int j = sub; j < n; j += tpr) {
       if (intree ? !((mwt >> ((t0 + j) & 63)) & 1) : t0 + j < first) continue;
       float s = 0.f;
 #pragma unroll
@@ -142,7 +148,19 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
     }
   }
 
-  if (!active) return;
+  // join the tpr states of the row (consecutive lanes of one wavefront)
+  for (int off = 1; off < tpr; off <<= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    const float mn = fmaxf(m, mo);
+    const float a0 = m == -INFINITY ? 0.f : exp2f(m - mn);  // a state without keys weighs 0
+    const float a1 = mo == -INFINITY ? 0.f : exp2f(mo - mn);
+    l = l * a0 + lo * a1;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = acc[d] * a0 + __shfl_xor(acc[d], off) * a1;
+    m = mn;
+  }
+  if (!active || sub != 0) return;
   const size_t pr = (static_cast<size_t>(b * a.Hkv + g) * a.slots + slot) * a.R + r;  // active row
   const float inv = l > 0.f ? 1.f / l : 0.f;  // no keys: o = 0, lse = -inf
   float* op = static_cast<float*>(a.o_part) + pr * D;
@@ -153,12 +171,18 @@ __global__ __launch_bounds__(256) void partial_simple_kernel(PartialArgs a) {
 
 template <typename Tin>
 hipError_t launch_typed(const Plan& p, PartialArgs a, hipStream_t stream) {
-  const int rblocks = (p.R + kRowsPerWG - 1) / kRowsPerWG;
+  // threads per row: the largest power of two up to 32 that still fits all
+  // rows of a (sequence, KV head) into one workgroup, else 1
+  int tpr = 1;
+  while (tpr < 32 && p.R * tpr * 2 <= kThreadsWG) tpr *= 2;
+  a.simple_tpr = tpr;
+  const int rows_per_wg = kThreadsWG / tpr;
+  const int rblocks = (p.R + rows_per_wg - 1) / rows_per_wg;
   const dim3 grid(p.Hkv, p.slots, p.B * rblocks);
   if (p.D == 128) {
-    hipLaunchKernelGGL((partial_simple_kernel<Tin, 128>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((partial_simple_kernel<Tin, 128>), grid, dim3(kThreadsWG), 0, stream, a);
   } else {
-    hipLaunchKernelGGL((partial_simple_kernel<Tin, 64>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((partial_simple_kernel<Tin, 64>), grid, dim3(kThreadsWG), 0, stream, a);
   }
   return hipGetLastError();
 }

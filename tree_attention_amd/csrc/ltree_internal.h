@@ -84,6 +84,7 @@ struct PartialArgs {
   const int32_t* block_table;
   int page_size, max_pages, num_pages;
   int page_shift;    // log2(page_size) when it is a power of two, else -1
+  int simple_tpr;    // fp32 kernel: threads per query row (set by its launcher)
   float scale_log2;  // scale * log2(e)
   float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
   float neg_inv_scale_log2;  // -1 / scale_log2
