@@ -264,7 +264,7 @@ size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, i
  * every ancestor.  Otherwise as ltree_attn (scores, lse, GQA, fp32 outputs).
  *
  *   dtype, B, T, Hq, Hkv, D, scale, q, k_tree, v_tree, mask, o, lse, stream
- *                  as for ltree_attn, with T <= 64 (one mask word per row).
+ *                  as for ltree_attn.
  *   window         T <= window <= LTREE_MAX_WINDOW.
  *   k_cache, v_cache  [sum L_b, Hkv, D] packed by cache_offsets [B+1] (as
  *                  k_prefix/v_prefix of ltree_attn), not NULL; L_b may exceed
@@ -274,8 +274,7 @@ size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, i
  *   workspace      ltree_window_attn_workspace_bytes(B, T, Hq, Hkv, D, window)
  *                  bytes, 256-byte aligned, caller-owned.
  *
- * Returns as ltree_attn (LTREE_ERR_INVALID_ARG also for window < T,
- * LTREE_ERR_UNSUPPORTED for T > 64).  A
+ * Returns as ltree_attn (LTREE_ERR_INVALID_ARG also for window < T).  A
  * decreasing cache_offsets table (L_b < 0) turns that sequence's rows into
  * NaN.  Two kernel launches.
  */

@@ -2,7 +2,7 @@
 through the C ABI, against the fp64 oracle: the mask bit-exact, attention
 within the stated tolerances (several tree tiles per sequence, several row
 blocks per KV head), RoPE within one unit in the last place, the commit
-bit-exact; window attention rejects them."""
+bit-exact, window attention within the tolerances."""
 
 import zlib
 
@@ -147,18 +147,31 @@ def test_commit_wide_tree():
     assert np.array_equal(as16(kc_d.cpu()), rk) and np.array_equal(as16(vc_d.cpu()), rv)
 
 
-def test_window_rejects_wide_tree():
+@pytest.mark.parametrize("name,B,T,lens,trees,dtype,window", [
+    ("w512_chain80_short_cache", 1, 80, [100], "chain", "bf16", 512),
+    # chains of 200 / 130 nodes after long caches: the deepest rows hide 199 /
+    # 129 cache keys, across four / three 64-key splits
+    ("w256_chain200", 2, 200, [3000, 150], "chain", "bf16", 256),
+    ("w300_fp32_chain130", 2, 130, [500, 0], "chain", "f32", 300),
+    ("w256_t200_bounded", 1, 200, [1000], ("bounded", 40, 3), "bf16", 256),
+])
+def test_window_wide_tree(name, B, T, lens, trees, dtype, window):
+    """Window attention over trees above 64 nodes: rows hide up to depth - 1
+    cache keys, spread over several 64-key splits."""
     import tree_attention_amd as ta
-    rng = np.random.default_rng(13)
-    w = make_workload(rng, B=1, T=80, Hq=4, Hkv=2, D=128, prefix_lens=[100], trees="chain",
-                      dtype="bf16")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    w = make_workload(rng, B=B, T=T, Hq=8, Hkv=2, D=128, prefix_lens=lens, trees=trees,
+                      dtype=dtype, name=name)
     dev = "cuda"
     mask, _ = ta.build_mask(w.parent.to(dev))
-    o = torch.empty((1, 80, 4, 128), dtype=torch.float32, device=dev)
-    lse = torch.empty((1, 4, 80), dtype=torch.float32, device=dev)
-    ws = torch.empty((1 << 22,), dtype=torch.uint8, device=dev)
-    say("window rejects T > 64")
-    st = ta.ltree_window_attn(w.q.to(dev), w.k_prefix.to(dev), w.v_prefix.to(dev),
-                              w.offsets.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask, o,
-                              lse, ws, w.scale, 512)
-    assert st == ta.LTREE_ERR_UNSUPPORTED
+    say("window wide tree", name)
+    o, lse = ta.window_attn(w.q.to(dev), w.k_prefix.to(dev), w.v_prefix.to(dev),
+                            w.offsets.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask,
+                            w.scale, window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.oracle_window_attn(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(),
+                                               w.k_tree, w.v_tree, w.parent.numpy(), w.scale,
+                                               window)
+    tol = 2e-2 if dtype == "bf16" else 1e-4
+    assert np.max(np.abs(o.cpu().double().numpy() - o_ref)) <= tol
+    assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) <= LSE_TOL

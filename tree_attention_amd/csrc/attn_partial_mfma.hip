@@ -79,6 +79,7 @@ constexpr int kMaxTPW = 3;   // row tiles per wave at most (384 rows per workgro
 constexpr int kVtRow = 144;  // bytes per V^T row: 64 fp16 keys + 16 bytes of pitch
 constexpr int kMaskStash = LTREE_MAX_TREE * ((LTREE_MAX_TREE + 63) / 64) * 8;  // LDS bytes, BIGT
 constexpr int kPageStash = kMaxSplitPages * 4;  // LDS bytes, PAGED: the split's page numbers
+constexpr int kHeadKeys = 256;  // window: keys at the start of the range a row may hide
 // fourth word of a raw buffer descriptor (32-bit data format; no swizzle)
 constexpr int kBufferFlags = 0x00020000;
 
@@ -185,8 +186,10 @@ struct Ctx {
   int kfirst;           // key index (within the sequence) of this partial's first prefix key
   int npk;              // prefix keys of this partial
   bool tree;            // the tree keys follow them
-  bool head;            // sliding window, first split: its first tile is masked per row
-  int hbase;            // then row i sees keys hbase + depth(i) .. of that tile
+  bool head;            // sliding window, a split within the first 256 keys of the range:
+                        // its tiles there are masked per row
+  int hbase;            // row i sees keys hbase + depth(i) .. of the range
+  int hk0;              // the split's first key, counted from the start of the range
   int tid, lane, wave, l16, grp;
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
 };
@@ -236,10 +239,17 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
                     (static_cast<uint32_t>((mw >> (32 + 8 * grp)) & 0xffu) << 8);
       }
-      if (head) {  // bits 16..21: the row's first visible key of the head tile
+      if (head) {  // bits 16..23: the row's first visible key of the window
         const int sh = min(max(x.hbase + static_cast<int>(__popcll(mw)), 0), 63);
         vbits[rt] |= static_cast<uint32_t>(sh) << 16;
       }
+    }
+    if (BIGT && head && ok) {  // depth over the row's W mask words; up to 255 keys hidden
+      int depth = 0;
+      for (int w = 0; w < a.W; ++w) {
+        depth += static_cast<int>(__popcll(a.mask[(static_cast<size_t>(x.b) * a.T + i) * a.W + w]));
+      }
+      vbits[rt] |= static_cast<uint32_t>(min(max(x.hbase + depth, 0), 255)) << 16;
     }
   }
 
@@ -432,7 +442,8 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // S^T = K . Q^T for row tile rt; keys past the end, tree keys outside the
   // row's branch and, in the window's head tile, keys before the row's window
   // get -inf
-  auto qk = [&](f32x4 (&s)[2], int rt, int H, int valid, bool treeblk, bool headblk, auto MASK_) {
+  // hk >= 0: a window head tile whose first key is key hk of the range
+  auto qk = [&](f32x4 (&s)[2], int rt, int H, int valid, bool treeblk, int hk, auto MASK_) {
 #pragma unroll
     for (int c = 0; c < C::DC; ++c)
 #pragma unroll
@@ -445,8 +456,8 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       // whole loop
       const int nin = min(max(valid - 8 * grp, 0), 8);
       uint32_t bits = (!treeblk ? 0xffu : H ? (vbits[rt] >> 8) : vbits[rt]) & ((1u << nin) - 1u);
-      if (WIN && headblk) {  // this lane's keys are 32H + 8grp + 0..7 of the tile
-        const int sh = static_cast<int>(vbits[rt] >> 16) - (32 * H + 8 * grp);
+      if (WIN && hk >= 0) {  // this lane's keys are hk + 32H + 8grp + 0..7
+        const int sh = static_cast<int>(vbits[rt] >> 16) - (hk + 32 * H + 8 * grp);
         bits &= sh <= 0 ? 0xffu : sh >= 8 ? 0u : (0xffu << sh);
       }
       asm volatile("" : "+v"(bits));
@@ -506,11 +517,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   //
   // Row tile by row tile: the check of row tile rt, then its exponentials
   // with the QK products of row tile rt+1 in flight.
-  auto qk_softmax = [&](auto H_, int valid, bool treeblk, bool headblk, auto MASK_) {
+  auto qk_softmax = [&](auto H_, int valid, bool treeblk, int hk, auto MASK_) {
     constexpr int H = decltype(H_)::value;
     f32x4 s[2][2];
     float lm[2];
-    qk(s[0], 0, H, valid, treeblk, headblk, MASK_);
+    qk(s[0], 0, H, valid, treeblk, hk, MASK_);
     lm[0] = lane_max(s[0]);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
@@ -519,7 +530,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       probs(s[rt & 1], rt, bsum);
       lsum[rt] += bsum;
       if (rt + 1 < NT) {
-        qk(s[(rt + 1) & 1], rt + 1, H, valid, treeblk, headblk, MASK_);
+        qk(s[(rt + 1) & 1], rt + 1, H, valid, treeblk, hk, MASK_);
         lm[(rt + 1) & 1] = lane_max(s[(rt + 1) & 1]);
         // issue order: the products of row tile rt+1 one at a time between
         // the vector instructions of row tile rt
@@ -584,12 +595,15 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         for (int rt = 0; rt < NT; ++rt) {
           const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
           const uint64_t mw = r < x.rend ? mst[(r / a.G) * a.W + u] : ~0ull;
-          vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
+          vbits[rt] = (vbits[rt] & 0xffff0000u) |  // (keeps a window's first-key bits)
+                      static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
                       (static_cast<uint32_t>((mw >> (32 + 8 * grp)) & 0xffu) << 8);
         }
       }
     }
-    const bool hb = head && t == 0;
+    // window head tiles: those within the first 256 keys of the range (a row
+    // hides at most depth - 1 <= 255 of them; 63 for trees of up to 64 nodes)
+    const int hb = (head && !tt && x.hk0 + t * kTile < kHeadKeys) ? x.hk0 + t * kTile : -1;
     const bool more = t + 1 < ntiles;
     // both blocks always run: a block without real keys (the last tile may
     // hold 32 or fewer) is fully masked, its probabilities are zero
@@ -700,7 +714,6 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
 template <int D, int TPW, bool WIN, bool BIGT, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
-  static_assert(!(WIN && BIGT), "the window variant takes trees of at most 64 nodes");
   static_assert(!(WIN && PAGED), "the window variant reads a packed cache");
   __shared__ __attribute__((aligned(1024)))
   char smem[C::SMEM + (BIGT ? kMaskStash : 0) + (PAGED ? kPageStash : 0)];
@@ -731,9 +744,11 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.kfirst = start + k0;
   x.tree = a.has_tree && x.slot == nparts - 1;
   // window W: node i sees prefix keys from L - W + depth(i) on, i.e. from
-  // key n - W + depth(i) of the range, which lies in its first tile
-  x.head = a.window > 0 && x.slot == 0 && x.npk > 0;
+  // key n - W + depth(i) <= depth(i) - 1 of the range (within its first 64
+  // keys for trees of up to 64 nodes, its first 256 for larger ones)
+  x.head = a.window > 0 && x.npk > 0 && k0 < kHeadKeys;
   x.hbase = n - a.window;
+  x.hk0 = k0;
   x.kstride = a.Hkv * D;
   const size_t row0 = static_cast<size_t>(off0) + start + k0;
   x.kbase = static_cast<const __bf16*>(a.kp) + (row0 * a.Hkv + x.g) * D;
@@ -806,7 +821,10 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   a.row_blocks = (p.R + a.rows_per_wg - 1) / a.rows_per_wg;
   const dim3 grid(p.Hkv, p.slots, p.B * a.row_blocks);
   const bool big = a.T > 64;
-  if (a.window > 0) return launch_dd<true, false, false>(p.D, tpw, grid, a, stream);  // T <= 64
+  if (a.window > 0) {
+    return big ? launch_dd<true, true, false>(p.D, tpw, grid, a, stream)
+               : launch_dd<true, false, false>(p.D, tpw, grid, a, stream);
+  }
   if (a.block_table != nullptr) {
     return big ? launch_dd<false, true, true>(p.D, tpw, grid, a, stream)
                : launch_dd<false, false, true>(p.D, tpw, grid, a, stream);

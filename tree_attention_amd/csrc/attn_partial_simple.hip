@@ -96,12 +96,15 @@ __global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs 
 #pragma unroll
     for (int d = 0; d < D; ++d) qv[d] = active ? to_f32(qp[d]) * a.scale_log2 : 0.f;
   }
-  // this row's mask words (W per row; one when a window is used)
+  // this row's mask words (W per row)
   const uint64_t* mrow =
       a.mask != nullptr ? a.mask + (static_cast<size_t>(b) * a.T + i) * a.W : nullptr;
-  const uint64_t mw = (a.window > 0 && active) ? mrow[0] : 0ull;
+  int depth = 0;
+  if (a.window > 0 && active) {
+    for (int w = 0; w < a.W; ++w) depth += static_cast<int>(__popcll(mrow[w]));
+  }
   // window W: this row sees prefix keys from key n - W + depth(i) of the range
-  const int first = a.window > 0 ? n - a.window + static_cast<int>(__popcll(mw)) - k0 : 0;
+  const int first = a.window > 0 ? n - a.window + depth - k0 : 0;
 
   float m = -INFINITY, l = 0.f;
   float acc[D];

@@ -303,7 +303,6 @@ int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
     return LTREE_ERR_INVALID_ARG;
   }
   if (window < 1 || window < T) return LTREE_ERR_INVALID_ARG;
-  if (T > 64) return LTREE_ERR_UNSUPPORTED;  // one mask word per row
   if (window > LTREE_MAX_WINDOW) return LTREE_ERR_UNSUPPORTED;
   int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_cache, v_cache, cache_offsets,
                     window - 1, true, k_tree, v_tree, mask, workspace, workspace_bytes, stream,
