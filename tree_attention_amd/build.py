@@ -66,5 +66,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "ltree_c_caller.c")
+C_CALLER = os.path.join(ROOT, "tests", "c_abi", "ltree_c_caller")
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """Compile the plain C test caller of the library (host code only, gcc)
+    against include/ltree.h and libltree.so."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", INCLUDE, C_CALLER_SRC,
+           "-L", PKG, "-lltree", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../tree_attention_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_CALLER]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"gcc failed on the C caller:\n{res.stderr}")
+    return C_CALLER
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_caller(verbose="-v" in sys.argv))
