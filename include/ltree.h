@@ -221,7 +221,11 @@ size_t ltree_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, in
  *
  *   k_pages, v_pages  [num_pages, page_size, Hkv, D] page pools (dtype as q).
  *   num_pages         >= 1, pages in each pool.
- *   page_size         keys per page, a multiple of 64.
+ *   page_size         keys per page, >= 1.  A multiple of 64 (every 64-key tile
+ *                     within one page) takes any pool size; other page sizes
+ *                     address rows lane by lane from the start of the pool and
+ *                     need num_pages * page_size * Hkv * D * element bytes
+ *                     below 2^31 (else LTREE_ERR_UNSUPPORTED).
  *   block_table       [B, max_pages_per_seq] int32: key j of sequence b is row
  *                     j % page_size of page block_table[b, j / page_size].
  *                     Entries past a sequence's last page are not read.  A page

@@ -1,7 +1,8 @@
 """Tree-verification attention over a paged prefix cache on the GPU, through
 the C ABI: against the fp64 oracle on the gathered keys (`gather_paged`), and
 against the packed-layout call on the same keys.  Pages are shuffled through
-a pool with unused pages; page sizes 64 to 256; bf16 and fp32; D 64 and 128;
+a pool with unused pages; page sizes 16 to 256 (multiples of 64 and others);
+bf16 and fp32; D 64 and 128;
 trees up to and beyond 64 nodes; prefix-only mode; a page number outside the
 pool and a length above max_prefix_len give NaN rows for that sequence only."""
 
@@ -80,6 +81,11 @@ CASES = {
     "p256_fp32": (2, 16, 4, 2, 128, [300, 77], "forest", "f32", 256),
     "p64_bf16_t100": (2, 100, 8, 2, 128, [500, 64], ("bounded", 12, 4), "bf16", 64),
     "p192_bf16_g5": (1, 64, 10, 2, 128, [2000], ("bounded", 8, 3), "bf16", 192),
+    # page sizes that are not a multiple of 64: rows addressed lane by lane
+    "p16_bf16_ragged": (3, 32, 8, 2, 128, [700, 0, 131], ("bounded", 6, 4), "bf16", 16),
+    "p48_bf16_d64": (2, 17, 8, 2, 64, [1000, 129], "uniform", "bf16", 48),
+    "p16_bf16_t100": (2, 100, 8, 2, 128, [500, 64], ("bounded", 12, 4), "bf16", 16),
+    "p32_fp32": (2, 16, 4, 2, 128, [300, 77], "forest", "f32", 32),
 }
 
 
@@ -139,15 +145,16 @@ def test_paged_bad_page_and_length_give_nan_rows():
     assert np.max(np.abs(lse[1] - lse_ref[1])) <= LSE_TOL
 
 
-def test_paged_qwq_shape_matches_packed():
+@pytest.mark.parametrize("P", [256, 16])
+def test_paged_qwq_shape_matches_packed(P):
     """The QwQ-shaped layer (40/8 heads, D 128, prefix 32768, 64-node tree)
-    with 256-key pages shuffled through the pool: the same result as the
-    packed call, which the oracle checks elsewhere."""
+    with 256- and 16-key pages shuffled through the pool: the same result as
+    the packed call, which the oracle checks elsewhere."""
     import tree_attention_amd as ta
     from workloads import make_config
     w = make_config(4)
     rng = np.random.default_rng(31)
-    kp, vp, bt, lens = _paginate(w, 256, rng)
+    kp, vp, bt, lens = _paginate(w, P, rng)
     say("paged qwq shape")
     o, lse = _run(w, kp, vp, bt, lens)
     dev = "cuda"
@@ -164,14 +171,15 @@ def test_paged_argument_errors():
     w, P, rng = _case("p64_bf16_ragged")
     kp, vp, bt, lens = _paginate(w, P, rng)
     dev = "cuda"
-    assert ta.ltree_attn_paged_workspace_bytes(3, 32, 8, 2, 128, 700, 96) == 0   # not a multiple of 64
-    kp48 = torch.zeros(4, 48, 2, 128, dtype=torch.bfloat16, device=dev)
+    assert ta.ltree_attn_paged_workspace_bytes(3, 32, 8, 2, 128, 700, 0) == 0   # no page size
+    assert ta.ltree_attn_paged_workspace_bytes(3, 32, 8, 2, 128, 700, 48) > 0
+    kp0 = torch.zeros(4, 0, 2, 128, dtype=torch.bfloat16, device=dev)
     o = torch.empty((3, 32, 8, 128), dtype=torch.float32, device=dev)
     lse = torch.empty((3, 8, 32), dtype=torch.float32, device=dev)
     ws = torch.empty((1 << 24,), dtype=torch.uint8, device=dev)
     mask, _ = ta.build_mask(w.parent.to(dev))
     say("paged argument errors")
-    st = ta.ltree_attn_paged(w.q.to(dev), kp48, kp48, bt.to(dev), lens.to(dev), 700,
+    st = ta.ltree_attn_paged(w.q.to(dev), kp0, kp0, bt.to(dev), lens.to(dev), 700,
                              w.k_tree.to(dev), w.v_tree.to(dev), mask, o, lse, ws, w.scale)
     assert st == ta.LTREE_ERR_INVALID_ARG
     # max_prefix_len beyond what the block table can address

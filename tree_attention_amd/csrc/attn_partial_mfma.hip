@@ -201,9 +201,11 @@ struct Ctx {
 // each row tile reads from a copy of the sequence's mask words in LDS at the
 // start of the tile (W = ceil(T/64) words per row).
 // PAGED: the prefix keys live in pages of a shared pool; the page numbers of
-// the split are copied to LDS first, and each 64-key tile (never across a
-// page boundary: the page size is a multiple of 64) gets its own base.
-template <int D, int NT, bool WIN, bool BIGT, bool PAGED>
+// the split are copied to LDS first.  PAGED == 1 (page size a multiple of
+// 64): each 64-key tile lies in one page and gets its own base.  PAGED == 2
+// (any page size, a pool below 4 GB): one buffer spans the pool and every
+// lane finds its own row's page.
+template <int D, int NT, bool WIN, bool BIGT, int PAGED>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
@@ -342,6 +344,15 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // PAGED: the split's page numbers in LDS (after the mask words, if any)
   const int32_t* pst = reinterpret_cast<const int32_t*>(sm + C::SMEM + (BIGT ? kMaskStash : 0));
   const int p0 = PAGED ? (a.page_shift >= 0 ? x.kfirst >> a.page_shift : x.kfirst / a.page_size) : 0;
+  // PAGED == 2: pool row of the split's key k (relative to kfirst), from the
+  // LDS page table
+  auto pool_row = [&](int k) -> uint32_t {
+    const int key = x.kfirst + k;
+    const int slot = a.page_shift >= 0 ? key >> a.page_shift : key / a.page_size;
+    const int in_page = a.page_shift >= 0 ? key & (a.page_size - 1) : key % a.page_size;
+    return static_cast<uint32_t>(pst[slot - p0]) * static_cast<uint32_t>(a.page_size) +
+           static_cast<uint32_t>(in_page);
+  };
   auto dma = [&](int S, int t) {
     const bool tt = BIGT ? t >= ptiles : t == ptiles;  // a tree tile
     const int u = BIGT ? t - ptiles : 0;                // its index among the tree tiles
@@ -351,7 +362,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const int bytes = nrows * kstride * 2;
     const __bf16* kb = (tt ? x.ktree : x.kbase) + toff;
     const __bf16* vb = (tt ? x.vtree : x.vbase) + toff;
-    if constexpr (PAGED) {
+    if constexpr (PAGED == 2) {
+      if (!tt) {  // one buffer over the pool (from KV head g on); rows by lane below
+        kb = static_cast<const __bf16*>(a.kp) + x.g * D;
+        vb = static_cast<const __bf16*>(a.vp) + x.g * D;
+      }
+    }
+    if constexpr (PAGED == 1) {
       if (!tt) {  // tile t: keys kfirst + 64t .. of page pst[(kfirst + 64t) / P - p0]
         const int key = x.kfirst + t * kTile;
         const int slot = a.page_shift >= 0 ? key >> a.page_shift : key / a.page_size;
@@ -362,12 +379,22 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         vb = static_cast<const __bf16*>(a.vp) + row * kstride + x.g * D;
       }
     }
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kb), 0, bytes, kBufferFlags);
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vb), 0, bytes, kBufferFlags);
+    const bool lane_rows = PAGED == 2 && !tt;
+    const int range = lane_rows ? static_cast<int>(a.pool_bytes - static_cast<uint32_t>(x.g * D * 2)) : bytes;
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kb), 0, range, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vb), 0, range, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < C::KDMA; ++j) {
       char* dst = sm + Cfg<D>::K0 + S * Cfg<D>::BUF + (j * kWaves + wave) * 1024;
-      const int vo = ksoff[j];
+      int vo = ksoff[j];
+      if constexpr (PAGED == 2) {
+        if (lane_rows) {  // rows past the tile's last key repeat it (they are masked)
+          const int row = (j * kWaves + wave) * C::ROWS_PER_DMA + lane / C::KC16;
+          const uint32_t pr = pool_row(t * kTile + min(row, nrows - 1));
+          vo = static_cast<int>((pr * static_cast<uint32_t>(kstride) +
+                                 static_cast<uint32_t>(((lane % C::KC16) ^ kswz<D>(row)) * 8)) * 2u);
+        }
+      }
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)dst, 16, vo, 0, 0, 0);
     }
     if (vstage) {
@@ -377,7 +404,14 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
         for (int j = 0; j < 2; ++j) {
           char* dst = sm + Cfg<D>::R0 + S * Cfg<D>::BUF +
                       (j * (Cfg<D>::VITEMS / 64) + i * kWaves + wave) * 1024;
-          const int vo = vsoff[i][j];
+          int vo = vsoff[i][j];
+          if constexpr (PAGED == 2) {
+            if (lane_rows) {
+              const int it = tid + i * kThreads, vm = it / C::KC16, vc = it % C::KC16;
+              const uint32_t pr = pool_row(min(t * kTile + 2 * vm + j, t * kTile + nrows - 1));
+              vo = static_cast<int>((pr * static_cast<uint32_t>(kstride) + static_cast<uint32_t>(vc * 8)) * 2u);
+            }
+          }
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)dst, 16, vo, 0, 0, 0);
         }
     }
@@ -711,7 +745,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
 }
 
-template <int D, int TPW, bool WIN, bool BIGT, bool PAGED>
+template <int D, int TPW, bool WIN, bool BIGT, int PAGED>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
   static_assert(!(WIN && PAGED), "the window variant reads a packed cache");
@@ -781,7 +815,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   run<D, 1, WIN, BIGT, PAGED>(x);  // one tile, or none: a wave without rows still stages and syncs
 }
 
-template <int D, bool WIN, bool BIGT, bool PAGED>
+template <int D, bool WIN, bool BIGT, int PAGED>
 hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   switch (tpw) {
     case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
@@ -791,7 +825,7 @@ hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool WIN, bool BIGT, bool PAGED>
+template <bool WIN, bool BIGT, int PAGED>
 hipError_t launch_dd(int D, int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   return D == 128 ? launch_d<128, WIN, BIGT, PAGED>(tpw, grid, a, stream)
                   : launch_d<64, WIN, BIGT, PAGED>(tpw, grid, a, stream);
@@ -822,15 +856,19 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   const dim3 grid(p.Hkv, p.slots, p.B * a.row_blocks);
   const bool big = a.T > 64;
   if (a.window > 0) {
-    return big ? launch_dd<true, true, false>(p.D, tpw, grid, a, stream)
-               : launch_dd<true, false, false>(p.D, tpw, grid, a, stream);
+    return big ? launch_dd<true, true, 0>(p.D, tpw, grid, a, stream)
+               : launch_dd<true, false, 0>(p.D, tpw, grid, a, stream);
   }
-  if (a.block_table != nullptr) {
-    return big ? launch_dd<false, true, true>(p.D, tpw, grid, a, stream)
-               : launch_dd<false, false, true>(p.D, tpw, grid, a, stream);
+  if (a.block_table != nullptr && a.page_size % kTile == 0) {  // whole tiles per page
+    return big ? launch_dd<false, true, 1>(p.D, tpw, grid, a, stream)
+               : launch_dd<false, false, 1>(p.D, tpw, grid, a, stream);
   }
-  return big ? launch_dd<false, true, false>(p.D, tpw, grid, a, stream)
-             : launch_dd<false, false, false>(p.D, tpw, grid, a, stream);
+  if (a.block_table != nullptr) {  // rows by lane (a pool below 4 GB)
+    return big ? launch_dd<false, true, 2>(p.D, tpw, grid, a, stream)
+               : launch_dd<false, false, 2>(p.D, tpw, grid, a, stream);
+  }
+  return big ? launch_dd<false, true, 0>(p.D, tpw, grid, a, stream)
+             : launch_dd<false, false, 0>(p.D, tpw, grid, a, stream);
 }
 
 }  // namespace ltree

@@ -32,7 +32,7 @@ int device_cu_count() {
 
 bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window,
                int page_size) {
-  if (page_size < 0 || page_size % 64 != 0) return false;
+  if (page_size < 0) return false;
   if (window < 0 || window > LTREE_MAX_WINDOW || (window > 0 && window < T)) return false;
   if (window > 0) max_prefix_len = window - 1;
   if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) return false;
@@ -70,7 +70,7 @@ bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p
   // a paged split's page numbers fit the kernels' LDS table (a split that
   // starts inside a page touches one page more than it fills)
   if (page_size > 0 && chunk > static_cast<long>(kMaxSplitPages - 1) * page_size) {
-    chunk = static_cast<long>(kMaxSplitPages - 1) * page_size;
+    chunk = static_cast<long>(kMaxSplitPages - 1) * page_size / 64 * 64;
   }
   if (chunk < 64) return false;
   p->chunk = static_cast<int>(chunk);
@@ -138,6 +138,7 @@ struct Paging {
   const int32_t* seq_lens = nullptr;
   const int32_t* block_table = nullptr;
   int page_size = 0, max_pages = 0, num_pages = 0;
+  uint32_t pool_bytes = 0;
 };
 
 // Partials of prefix (+ tree, when has_tree) attention into the workspace;
@@ -206,6 +207,7 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
   a.page_size = pg.page_size;
   a.max_pages = pg.max_pages;
   a.num_pages = pg.num_pages;
+  a.pool_bytes = pg.pool_bytes;
   a.page_shift = -1;
   if (pg.page_size > 0 && (pg.page_size & (pg.page_size - 1)) == 0) {
     a.page_shift = __builtin_ctz(static_cast<unsigned>(pg.page_size));
@@ -315,7 +317,7 @@ int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
 size_t ltree_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len,
                                         int page_size) {
   Plan p;
-  if (page_size < 64) return 0;
+  if (page_size < 1) return 0;
   return ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, 0, page_size) ? p.bytes : 0;
 }
 
@@ -329,13 +331,18 @@ int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, fl
       block_table == nullptr || seq_lens == nullptr) {
     return LTREE_ERR_INVALID_ARG;
   }
-  if (page_size < 64 || page_size % 64 != 0 || num_pages < 1 || max_pages_per_seq < 1 ||
+  if (page_size < 1 || num_pages < 1 || max_pages_per_seq < 1 ||
       max_prefix_len < 0 ||
       static_cast<long>(max_prefix_len) > static_cast<long>(max_pages_per_seq) * page_size) {
     return LTREE_ERR_INVALID_ARG;
   }
   // page rows are addressed with 64-bit offsets; a page's rows with 32-bit ones
   if (static_cast<long>(page_size) * Hkv * D > (1L << 30)) return LTREE_ERR_UNSUPPORTED;
+  // a page size that is not a multiple of 64 addresses every row from the
+  // start of the pool with a 32-bit byte offset
+  const long pool_bytes = static_cast<long>(num_pages) * page_size * Hkv * D *
+                          (dtype == LTREE_BF16 ? 2 : 4);
+  if (page_size % 64 != 0 && pool_bytes >= (1L << 31)) return LTREE_ERR_UNSUPPORTED;
   const bool has_tree = k_tree != nullptr || v_tree != nullptr || mask != nullptr;
   Paging pg;
   pg.seq_lens = seq_lens;
@@ -343,6 +350,7 @@ int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, fl
   pg.page_size = page_size;
   pg.max_pages = max_pages_per_seq;
   pg.num_pages = num_pages;
+  pg.pool_bytes = static_cast<uint32_t>(pool_bytes < (1L << 31) ? pool_bytes : 0);
   int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_pages, v_pages, nullptr, max_prefix_len,
                     has_tree, k_tree, v_tree, mask, workspace, workspace_bytes, stream, 0, pg);
   if (st != LTREE_OK) return st;

@@ -31,8 +31,8 @@ constexpr int kMaxSplitPages = 448;
 // Returns false when the sizes are invalid (the caller reports the status).
 // With window > 0 the prefix part of each sequence is at most its last
 // window - 1 keys, and max_prefix_len is taken as window - 1.
-// page_size > 0: a paged prefix; splits are capped so their pages fit the
-// kernels' LDS table.
+// page_size > 0: a paged prefix (any page size); splits are capped so their
+// pages fit the kernels' LDS table.
 bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window = 0,
                int page_size = 0);
 
@@ -84,6 +84,7 @@ struct PartialArgs {
   const int32_t* block_table;
   int page_size, max_pages, num_pages;
   int page_shift;    // log2(page_size) when it is a power of two, else -1
+  uint32_t pool_bytes;  // bytes of one pool when page_size is not a multiple of 64 (< 4 GB)
   int simple_tpr;    // fp32 kernel: threads per query row (set by its launcher)
   float scale_log2;  // scale * log2(e)
   float headroom;    // 15 / scale_log2: raw-score margin of the lazy softmax reference
