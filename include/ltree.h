@@ -289,6 +289,32 @@ int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
                       size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ltree_window_attn_paged_workspace_bytes -- bytes of workspace
+ * ltree_window_attn_paged needs (0 when the sizes are invalid).
+ */
+size_t ltree_window_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window,
+                                               int page_size);
+
+/*
+ * ltree_window_attn_paged -- ltree_window_attn over a paged draft cache: the
+ * window rule of ltree_window_attn, the cache addressed as in
+ * ltree_attn_paged (k_pages, v_pages, num_pages, page_size, block_table,
+ * max_pages_per_seq, seq_lens; only the last min(L_b, window - 1) keys of
+ * each sequence are read, so only their pages need valid entries).  A window
+ * starts at any key, so rows are addressed lane by lane from the start of the
+ * pool: num_pages * page_size * Hkv * D * element bytes must stay below 2^31
+ * (else LTREE_ERR_UNSUPPORTED).  The workspace is
+ * ltree_window_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, window, page_size)
+ * bytes.  Returns as ltree_window_attn.  Two kernel launches.
+ */
+int ltree_window_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                            int window, const void* q, const void* k_pages, const void* v_pages,
+                            int num_pages, int page_size, const int32_t* block_table,
+                            int max_pages_per_seq, const int32_t* seq_lens, const void* k_tree,
+                            const void* v_tree, const uint64_t* mask, float* o, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * ltree_commit_kv -- copy the keys and values of the accepted draft tokens from
  * the tree buffers into the KV cache, so they join the cached prefix of the
  * next verification step (gist.science page, opening explanation: the target

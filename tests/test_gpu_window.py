@@ -149,3 +149,36 @@ def test_window_shorter_than_tree_is_rejected():
                               w.offsets.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask, o,
                               lse, ws, w.scale, 15)
     assert st == ta.LTREE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("P,name", [(16, "w200_ragged_empty"), (64, "w512_eight_splits"),
+                                    (48, "w90_fp32_d128"), (32, "w_just_past_cache")])
+def test_window_over_paged_cache(P, name):
+    """The draft cache in pages shuffled through a pool: the same result as
+    the packed window call, and the oracle's on the gathered keys."""
+    import tree_attention_amd as ta
+    from test_gpu_paged import _paginate
+    w, window = _case(name)
+    rng = np.random.default_rng(P)
+    kp, vp, bt, lens = _paginate(w, P, rng)
+    dev = "cuda"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty((ta.ltree_window_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, window, P),),
+                     dtype=torch.uint8, device=dev)
+    say("window attn paged", name, P)
+    assert ta.ltree_window_attn_paged(w.q.to(dev), kp.to(dev), vp.to(dev), bt.to(dev),
+                                      lens.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask, o,
+                                      lse, ws, w.scale, window) == 0
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    o2, lse2 = _run(w, window)
+    assert np.max(np.abs(o - o2)) <= 1e-5 and np.max(np.abs(lse - lse2)) <= 1e-5
+    kg, off = oracle.gather_paged(kp.float().numpy(), bt.numpy(), lens.numpy(), P)
+    vg, _ = oracle.gather_paged(vp.float().numpy(), bt.numpy(), lens.numpy(), P)
+    o_ref, lse_ref = oracle.oracle_window_attn(w.q, kg, vg, off, w.k_tree, w.v_tree,
+                                               w.parent.numpy(), w.scale, window)
+    _check(w, o, lse, o_ref, lse_ref)

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
               "ltree_attn_partials", "ltree_attn_merge", "ltree_status_string",
               "ltree_version", "ltree_prefix_attn", "ltree_window_attn",
               "ltree_window_attn_workspace_bytes", "ltree_attn_paged",
-              "ltree_attn_paged_workspace_bytes", "ltree_tree_rope", "ltree_commit_kv"):
+              "ltree_attn_paged_workspace_bytes", "ltree_window_attn_paged",
+              "ltree_window_attn_paged_workspace_bytes", "ltree_tree_rope", "ltree_commit_kv"):
         assert n in names
 
 

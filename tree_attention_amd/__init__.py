@@ -33,6 +33,8 @@ from ._binding import (  # noqa: F401
     ltree_tree_rope,
     ltree_version,
     ltree_window_attn,
+    ltree_window_attn_paged,
+    ltree_window_attn_paged_workspace_bytes,
     ltree_window_attn_workspace_bytes,
     mask_shape,
     mask_words,

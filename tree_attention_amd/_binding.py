@@ -31,7 +31,8 @@ LTREE_MAX_TREE = 256
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
             "ltree_attn_merge", "ltree_prefix_attn", "ltree_attn_paged_workspace_bytes",
-            "ltree_attn_paged", "ltree_window_attn_workspace_bytes",
+            "ltree_attn_paged", "ltree_window_attn_paged_workspace_bytes",
+            "ltree_window_attn_paged", "ltree_window_attn_workspace_bytes",
             "ltree_window_attn", "ltree_commit_kv", "ltree_tree_rope")
 
 
@@ -60,6 +61,9 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_paged_workspace_bytes": (S, [I, I, I, I, I, I, I]),
         "ltree_attn_paged": (I, [I, I, I, I, I, I, F, P, P, P, I, I, P, I, P, I, P, P, P, P, P, P,
                                  S, P]),
+        "ltree_window_attn_paged_workspace_bytes": (S, [I, I, I, I, I, I, I]),
+        "ltree_window_attn_paged": (I, [I, I, I, I, I, I, F, I, P, P, P, I, I, P, I, P, P, P, P,
+                                        P, P, P, S, P]),
         "ltree_window_attn_workspace_bytes": (S, [I, I, I, I, I, I]),
         "ltree_window_attn": (I, [I, I, I, I, I, I, F, I, P, P, P, P, P, P, P, P, P, P, S, P]),
         "ltree_commit_kv": (I, [I, I, I, I, I, P, P, P, P, P, P, P, I, P, P]),
@@ -274,6 +278,44 @@ def ltree_attn_paged(q, k_pages, v_pages, block_table, seq_lens, max_prefix_len,
         _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(k_pages), _ptr(v_pages),
         num_pages, page_size, _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
         int(max_prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(o), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def ltree_window_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, window, page_size) -> int:
+    return int(_lib.ltree_window_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, int(window),
+                                                            int(page_size)))
+
+
+def ltree_window_attn_paged(q, k_pages, v_pages, block_table, seq_lens, k_tree, v_tree, mask, o,
+                            lse, workspace, scale, window, stream=None) -> int:
+    """Sliding-window self-attention of the tree tokens over a paged cache
+    (pools [num_pages, page_size, Hkv, D], block_table [B, max_pages],
+    seq_lens [B])."""
+    dt = q.dtype
+    for name, t in (("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("k_tree", k_tree),
+                    ("v_tree", v_tree)):
+        _dev(t, name, dt)
+    for name, t in (("block_table", block_table), ("seq_lens", seq_lens)):
+        _dev(t, name, torch.int32)
+    _dev(mask, "mask", torch.int64)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    B, T, Hq, D = q.shape
+    if k_pages.dim() != 4 or k_pages.shape[3] != D or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages/v_pages must be [num_pages, page_size, Hkv, D]")
+    num_pages, page_size, Hkv = k_pages.shape[:3]
+    if block_table.dim() != 2 or block_table.shape[0] != B or seq_lens.shape != (B,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    if k_tree.shape != (B, T, Hkv, D) or v_tree.shape != (B, T, Hkv, D):
+        raise ValueError("k_tree/v_tree must be [B, T, Hkv, D]")
+    _check_mask(mask, B, T)
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    return _lib.ltree_window_attn_paged(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), int(window), _ptr(q), _ptr(k_pages),
+        _ptr(v_pages), num_pages, page_size, _ptr(block_table), block_table.shape[1],
+        _ptr(seq_lens), _ptr(k_tree), _ptr(v_tree), _ptr(mask), _ptr(o), _ptr(lse),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
 
 

@@ -748,7 +748,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
 template <int D, int TPW, bool WIN, bool BIGT, int PAGED>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
-  static_assert(!(WIN && PAGED), "the window variant reads a packed cache");
+  static_assert(!(WIN && PAGED == 1), "a window starts anywhere: rows by lane over a paged cache");
   __shared__ __attribute__((aligned(1024)))
   char smem[C::SMEM + (BIGT ? kMaskStash : 0) + (PAGED ? kPageStash : 0)];
 
@@ -855,6 +855,10 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   a.row_blocks = (p.R + a.rows_per_wg - 1) / a.rows_per_wg;
   const dim3 grid(p.Hkv, p.slots, p.B * a.row_blocks);
   const bool big = a.T > 64;
+  if (a.window > 0 && a.block_table != nullptr) {  // a window starts anywhere: rows by lane
+    return big ? launch_dd<true, true, 2>(p.D, tpw, grid, a, stream)
+               : launch_dd<true, false, 2>(p.D, tpw, grid, a, stream);
+  }
   if (a.window > 0) {
     return big ? launch_dd<true, true, 0>(p.D, tpw, grid, a, stream)
                : launch_dd<true, false, 0>(p.D, tpw, grid, a, stream);

@@ -358,6 +358,47 @@ int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, fl
                workspace_bytes, stream, 0, pg);
 }
 
+size_t ltree_window_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window,
+                                               int page_size) {
+  Plan p;
+  if (window < 1 || page_size < 1) return 0;
+  return ltree::make_plan(B, T, Hq, Hkv, D, window - 1, &p, window, page_size) ? p.bytes : 0;
+}
+
+int ltree_window_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                            int window, const void* q, const void* k_pages, const void* v_pages,
+                            int num_pages, int page_size, const int32_t* block_table,
+                            int max_pages_per_seq, const int32_t* seq_lens, const void* k_tree,
+                            const void* v_tree, const uint64_t* mask, float* o, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (o == nullptr || lse == nullptr || k_pages == nullptr || v_pages == nullptr ||
+      block_table == nullptr || seq_lens == nullptr) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (window < 1 || window < T || page_size < 1 || num_pages < 1 || max_pages_per_seq < 1) {
+    return LTREE_ERR_INVALID_ARG;
+  }
+  if (window > LTREE_MAX_WINDOW) return LTREE_ERR_UNSUPPORTED;
+  if (static_cast<long>(page_size) * Hkv * D > (1L << 30)) return LTREE_ERR_UNSUPPORTED;
+  // a window starts at any key, so rows are addressed lane by lane from the
+  // start of the pool (32-bit byte offsets)
+  const long pool_bytes = static_cast<long>(num_pages) * page_size * Hkv * D *
+                          (dtype == LTREE_BF16 ? 2 : 4);
+  if (pool_bytes >= (1L << 31)) return LTREE_ERR_UNSUPPORTED;
+  Paging pg;
+  pg.seq_lens = seq_lens;
+  pg.block_table = block_table;
+  pg.page_size = page_size;
+  pg.max_pages = max_pages_per_seq;
+  pg.num_pages = num_pages;
+  pg.pool_bytes = static_cast<uint32_t>(pool_bytes);
+  int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_pages, v_pages, nullptr, window - 1,
+                    true, k_tree, v_tree, mask, workspace, workspace_bytes, stream, window, pg);
+  if (st != LTREE_OK) return st;
+  return merge(dtype, B, T, Hq, Hkv, D, nullptr, window - 1, o, lse, workspace, workspace_bytes,
+               stream, window, pg);
+}
+
 int ltree_commit_kv(ltree_dtype dtype, int B, int T, int Hkv, int D, const void* k_tree,
                     const void* v_tree, const int32_t* accepted, const int32_t* n_accepted,
                     const int32_t* dst_row, void* k_cache, void* v_cache, int cache_rows,
