@@ -43,7 +43,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "tree-verify attn µs/call + TFLOP/s @L=32k,T=64; % MFMA / HBM roofline"
-KERNEL_SOURCES = ["attn_partial_mfma.hip", "ltree_api.hip", "ltree_internal.h"]
+KERNEL_SOURCES = ["attn_partial_mfma_impl.h", "attn_partial_mfma.hip", "ltree_api.hip",
+                  "ltree_internal.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partials_qwq32b_L32k_T64.json")
 
 

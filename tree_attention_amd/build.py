@@ -19,6 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libltree.so")
 
 SOURCES = ["ltree_api.hip", "mask_build.hip", "attn_partial_mfma.hip",
+           "attn_partial_mfma_window.hip", "attn_partial_mfma_paged.hip",
            "attn_partial_simple.hip", "lse_merge.hip", "kv_commit.hip",
            "tree_rope.hip"]
 
@@ -33,7 +34,9 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # Per-file extras.  The partial-attention kernel never sees a NaN (inputs are
 # finite; masked scores are -inf), so NaN-quieting canonicalisation in front of
 # every float max can be dropped there.
-EXTRA_FLAGS = {"attn_partial_mfma.hip": ["-fno-honor-nans"]}
+EXTRA_FLAGS = {name: ["-fno-honor-nans"] for name in
+               ("attn_partial_mfma.hip", "attn_partial_mfma_window.hip",
+                "attn_partial_mfma_paged.hip")}
 
 
 def hipcc() -> str:
@@ -43,10 +46,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into tree_attention_amd/libltree.so."""
-    objs = []
-    for src in SOURCES:
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile every HIP source (in parallel, `jobs` at a time; 0 = one per
+    CPU up to 16) into tree_attention_amd/libltree.so."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    def compile_one(src):
         obj = os.path.join(CSRC, "_obj", src.replace(".hip", ".o"))
         os.makedirs(os.path.dirname(obj), exist_ok=True)
         cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
@@ -56,7 +61,11 @@ def build(verbose: bool = False) -> str:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")
-        objs.append(obj)
+        return obj
+
+    jobs = jobs or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
