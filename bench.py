@@ -86,9 +86,11 @@ def algorithmic_counts(w):
     return flop_prefix + flop_tree, bytes_, bytes_partials
 
 
-def cpu_baseline(w, budget_s=15.0):
-    """fp64 oracle on the first KV heads of the same workload, as many heads as
-    fit in about `budget_s` seconds (at least one)."""
+def cpu_baseline(w, budget_s=15.0, min_s=10.0):
+    """fp64 oracle on the same workload, one KV head (with its query heads) at
+    a time, for about `budget_s` seconds: as many heads as fit, and when the
+    whole layer takes less than `min_s`, whole passes over it repeated until
+    `min_s` have gone by (at least one head)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -99,27 +101,34 @@ def cpu_baseline(w, budget_s=15.0):
     G = Hq // Hkv
     parent = w.parent.numpy()
     off = w.offsets.numpy()
-    done, flop, t_total = 0, 0, 0.0
-    while done < Hkv and t_total < budget_s:
-        g = done
+    head_flop = 4 * D * G * T * sum(w.prefix_lens) + 4 * D * G * sum(
+        depth_sum(parent[b].tolist()) for b in range(B))
+    heads, flop, t_total, next_log = 0, 0, 0.0, 0.0
+    while heads == 0 or (t_total < budget_s and (heads % Hkv != 0 or t_total < min_s)):
+        g = heads % Hkv
         sl = slice(g, g + 1)
         t0 = time.perf_counter()
         oracle.oracle_attn(w.q[:, :, g * G:(g + 1) * G], w.k_prefix[:, sl], w.v_prefix[:, sl],
                            off, w.k_tree[:, :, sl], w.v_tree[:, :, sl], parent, w.scale)
         t_total += time.perf_counter() - t0
-        done += 1
-        flop += 4 * D * G * T * sum(w.prefix_lens) + 4 * D * G * sum(
-            depth_sum(parent[b].tolist()) for b in range(B))
-        log(f"cpu oracle: {done}/{Hkv} KV heads, {t_total:.1f} s")
+        heads += 1
+        flop += head_flop
+        if t_total >= next_log:  # a progress line every few seconds
+            log(f"cpu oracle: {heads} KV-head evaluations ({heads / Hkv:.2f} layers), "
+                f"{t_total:.1f} s")
+            next_log = t_total + 3.0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    passes = heads / Hkv
+    what = (f"{heads // Hkv} full passes over the layer" if heads % Hkv == 0
+            else f"{heads} of {Hkv} KV heads")
     return {
         "value": round(flop / t_total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 NumPy oracle over {done} of {Hkv} KV heads ({done * G} of {Hq} query "
-                  f"heads, all {T} tree rows, full {sum(w.prefix_lens)}-key prefix), "
-                  f"{t_total:.2f} s wall; matmuls on {threads} BLAS threads, exp single-threaded",
+        "sample": f"fp64 NumPy oracle, {what} ({passes:.2f} x {Hkv} KV heads, {Hq} query heads, "
+                  f"all {T} tree rows, full {sum(w.prefix_lens)}-key prefix), {t_total:.2f} s "
+                  f"wall; matmuls on {threads} BLAS threads, exp single-threaded",
     }
 
 
