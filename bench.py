@@ -13,8 +13,10 @@ whole call (wall clock over the timed steps, launched as one HIP graph;
 `us_per_call_eager` gives the same steps launched call by call); `roofline`
 rates the dominant kernel (the partial-attention kernel) against the bf16
 MFMA peak, with its duration taken from HIP events recorded on the launch
-stream around one replay of a graph of K launches of it on the same rotating
-inputs.  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
+stream around replays of a graph of K launches of it on the same rotating
+inputs (median over the replays).  `us_per_call_spread` adds the median and
+minimum per call over further replays of the timed graph, and the same steps
+over a single KV copy that stays in the Infinity Cache (hot cache, labelled).  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
 workload on the host cores.
 
 `--row NAME` measures one of the steps around the verification path instead
@@ -34,6 +36,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -42,6 +45,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+REPS = 7                    # extra replays of the timed graphs for median / minimum
 METRIC = "tree-verify attn µs/call + TFLOP/s @L=32k,T=64; % MFMA / HBM roofline"
 KERNEL_SOURCES = ["attn_partial_mfma_impl.h", "attn_partial_mfma.hip", "ltree_api.hip",
                   "ltree_internal.h"]
@@ -591,13 +595,32 @@ def main():
     o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
 
-    def partials(s):
-        kp, vp = kv[s % n_copies]
+    def partials(s, copies=n_copies):
+        kp, vp = kv[s % copies]
         return ta.ltree_attn_partials(q, kp, vp, offsets, max_l, kt, vt, mask, ws, w.scale)
 
-    def step(s):
-        return partials(s) | ta.ltree_attn_merge(q.dtype, B, T, Hq, Hkv, D, offsets, max_l, o,
-                                                 lse, ws)
+    def step(s, copies=n_copies):
+        return partials(s, copies) | ta.ltree_attn_merge(q.dtype, B, T, Hq, Hkv, D, offsets,
+                                                         max_l, o, lse, ws)
+
+    def replay_us(g, reps, events=False):
+        """Per-launch microseconds of `reps` timed replays of a graph of K
+        launches: wall clock around replay + synchronize, or HIP events on
+        the launch stream."""
+        out = []
+        for _ in range(reps):
+            if events:
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                out.append(e0.elapsed_time(e1) * 1000 / K)
+            else:
+                t0 = time.perf_counter()
+                g.replay()
+                torch.cuda.synchronize()
+                out.append((time.perf_counter() - t0) * 1e6 / K)
+        return out
 
     log(f"warmup {args.warmup} steps")
     for s in range(args.warmup):
@@ -629,6 +652,19 @@ def main():
     t1 = time.perf_counter()
     ms_per_step_eager = (t1 - t0) * 1000 / K
 
+    # the spread: the same graph replayed REPS more times (median and minimum
+    # per call over the replays), and the same K steps over one KV copy, so
+    # that the keys stay in the Infinity Cache (the hot-cache figure)
+    cold_us = replay_us(steps_graph, REPS)
+    hot_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(hot_graph):
+        for s in range(K):
+            step(s, 1)
+    hot_graph.replay()
+    torch.cuda.synchronize()
+    hot_us = replay_us(hot_graph, REPS)
+    del hot_graph
+
     # the dominant kernel alone: K launches of it captured in a graph and
     # replayed between two events on the launch stream (events around every
     # launch would add a cache flush to each; eager launches add the host's
@@ -639,11 +675,8 @@ def main():
             partials(s)
     part_graph.replay()
     torch.cuda.synchronize()
-    e0.record()
-    part_graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    part_us = e0.elapsed_time(e1) * 1000 / K
+    part_all = replay_us(part_graph, REPS, events=True)
+    part_us = statistics.median(part_all)
 
     us = ms_per_step * 1000
     tflops = flop / (us * 1e-6) / 1e12
@@ -674,6 +707,14 @@ def main():
         },
         "us_per_call": round(us, 2),
         "us_per_call_eager": round(ms_per_step_eager * 1000, 2),
+        "us_per_call_spread": {
+            "replays": REPS,
+            "cold_median": round(statistics.median(cold_us), 2),
+            "cold_min": round(min(cold_us), 2),
+            "hot_median": round(statistics.median(hot_us), 2),
+            "hot_min": round(min(hot_us), 2),
+            "hot_tflops": round(flop / (statistics.median(hot_us) * 1e-6) / 1e12, 2),
+        },
         "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
         "hbm_frac": round(bytes_alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "mask_build_us": round(mask_us, 2),
@@ -687,6 +728,7 @@ def main():
             "frac": round(part_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_us": round(part_us, 2),
+            "kernel_us_min": round(min(part_all), 2),
             "hbm_frac": round(bytes_partials / (part_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },
     }

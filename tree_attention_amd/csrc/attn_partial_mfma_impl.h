@@ -108,6 +108,8 @@ struct Cfg {
   static constexpr int VTHREADS = VITEMS / VIPT;          // threads that stage V
   static constexpr int DPT_V = KDMA + 2 * VIPT;           // DMA per tile, V-staging threads
   static constexpr int DPT_K = KDMA;                      // DMA per tile, other threads
+  static constexpr int OUT_PITCH = 2 * D + 16;            // LDS bytes per partial row (epilogue)
+  static_assert(kMaxTPW * kWaves * 16 * OUT_PITCH <= SMEM, "the partial rows fit in LDS");
 };
 
 // K rows: the 16 lanes of one lane group read keys 8a + b (+4), a, b in 0..3,
@@ -721,7 +723,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // (the 16-bit form halves the partials' memory traffic; its error is at most
   // 2^-16 of the row's largest magnitude).  Row r's D features are spread
   // over the four lane groups, so the max takes a reduction across them.
+  // The workgroup's rows are consecutive in the partial buffer: they are
+  // gathered in LDS (free once every wave is past its last tile) and leave
+  // as whole 16-byte chunks, each store instruction covering 1 KB of
+  // contiguous memory (written from the MFMA layout directly, a store would
+  // cover 16 separate 32-byte pieces).
   const size_t pbase = (static_cast<size_t>(x.b * a.Hkv + x.g) * a.slots + x.slot) * a.R;
+  lds_barrier();
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     const float l = group_sum(lsum[rt]);
@@ -734,19 +742,26 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const float inv = mx > 0.f ? 1.f / mx : 0.f;
     const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
     if (r < x.rend) {
-      int16_t* op = static_cast<int16_t*>(a.o_part) + (pbase + r) * D + 4 * grp;
+      char* ob = sm + (r - x.rbase) * C::OUT_PITCH + 8 * grp;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
         const f32x4 v = acc[dt][rt] * inv;
         const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(v[0], v[1]));
         const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pknorm_i16(v[2], v[3]));
-        *reinterpret_cast<u32x2*>(op + dt * 16) = (u32x2){lo, hi};
+        *reinterpret_cast<u32x2*>(ob + dt * 32) = (u32x2){lo, hi};
       }
       if (grp == 0) {
         a.lse_part[pbase + r] = -nmc[rt] + __builtin_amdgcn_logf(l);
         a.scale_part[pbase + r] = l > 0.f ? mx / l : 0.f;
       }
     }
+  }
+  lds_barrier();
+  char* const og = reinterpret_cast<char*>(static_cast<int16_t*>(a.o_part) + (pbase + x.rbase) * D);
+  const int nchunks = (x.rend - x.rbase) * C::KC16;
+  for (int k = tid; k < nchunks; k += kThreads) {
+    const int rr = k / C::KC16, c = k % C::KC16;
+    *reinterpret_cast<u32x4*>(og + 16 * k) = *reinterpret_cast<const u32x4*>(sm + rr * C::OUT_PITCH + 16 * c);
   }
 }
 
