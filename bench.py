@@ -25,7 +25,11 @@ self-attention, verification of a 256-node tree, verification over a paged
 cache, the KV-cache commit, the tree rotary embedding) and prints that row's
 own JSON line.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config 4]
+The default warm-up (1000 untimed steps, about 75 ms) lets the GPU settle
+at its sustained clocks; with 10 warm-up steps the timed steps run about 15%
+slower than the same steps a few tens of milliseconds later.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config 4]
     python bench.py --row {xattn,window,bigtree,paged,commit,rope}
 """
 
@@ -515,7 +519,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--hot", action="store_true", help="reuse one KV copy (cache-resident)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
