@@ -277,24 +277,25 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   //         key: far above any real offset, so the first key moves the
   //         reference and scales the empty accumulator by 2^-kNoRef = 0,
   //         and masked scores still give 2^-inf = 0, never inf - inf),
-  //   thr   m + 15/c2 = -nmc/c2 + 15/c2, formed when needed: a score above
-  //         it would give a probability above 2^15 (fp16 holds up to 65504),
+  //   thr   m + 15/c2 = -nmc/c2 + 15/c2, updated with the reference: a score
+  //         above it would give a probability above 2^15 (fp16 holds up to
+  //         65504),
   //   lsum  sum of this lane's probabilities as rounded to fp16 for P.V (the
   //         output is normalised by the same values it accumulates).
   constexpr float kNoRef = 1e30f;
   f32x4 acc[C::DT][NT];
-  float nmc[NT], lsum[NT];
+  float nmc[NT], lsum[NT], thr[NT];
+  const float c2 = a.scale_log2;
+  const float t8 = a.headroom;             // 15 / c2
+  const float nic2 = a.neg_inv_scale_log2;  // -1 / c2
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     nmc[rt] = kNoRef;
+    thr[rt] = fmaf(kNoRef, nic2, t8);
     lsum[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt][rt] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
-  const float c2 = a.scale_log2;
-  const float t8 = a.headroom;             // 15 / c2
-  const float nic2 = a.neg_inv_scale_log2;  // -1 / c2
-  auto thr = [&](int rt) { return fmaf(nmc[rt], nic2, t8); };
   // prefix tiles, then the tree tiles (one for T <= 64)
   const int ptiles = (npk + kTile - 1) / kTile;
   const int ntiles = ptiles + (tree ? (BIGT ? (T + kTile - 1) / kTile : 1) : 0);
@@ -512,18 +513,17 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   };
   // p = 2^(s*c2 - m*c2) in fp16 for P.V, and their sum (the same fp16
   // values, accumulated in fp32)
-  auto probs = [&](const f32x4 (&s)[2], int rt, float& bsum) {
+  auto probs = [&](const f32x4 (&s)[2], int rt) {
     float p[8];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int v = 0; v < 4; ++v) p[4 * sub + v] = __builtin_amdgcn_exp2f(fmaf(s[sub][v], c2, nmc[rt]));
     f16x2 hp[4];
-    bsum = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       hp[k] = __builtin_convertvector((f32x2){p[2 * k], p[2 * k + 1]}, f16x2);
-      bsum = add_f16x2(hp[k], bsum);
+      lsum[rt] = add_f16x2(hp[k], lsum[rt]);
     }
     P[rt] = __builtin_bit_cast(f16x8, (u32x4){__builtin_bit_cast(uint32_t, hp[0]),
                                               __builtin_bit_cast(uint32_t, hp[1]),
@@ -540,10 +540,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // passed the threshold, and rescale what it has accumulated.
   auto rescale = [&](int rt, float lm) {
     const float mt = group_max(lm);
-    const bool up = mt > thr(rt);  // this row's reference moves to mt
+    const bool up = mt > thr[rt];  // this row's reference moves to mt
     const float n_new = up ? -mt * c2 : nmc[rt];
     const float alpha = up ? __builtin_amdgcn_exp2f(n_new - nmc[rt]) : 1.f;
     nmc[rt] = n_new;
+    thr[rt] = fmaf(n_new, nic2, t8);
     lsum[rt] *= alpha;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) acc[dt][rt] *= alpha;
@@ -566,10 +567,8 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     lm[0] = lane_max(s[0]);
 #pragma unroll
     for (int rt = 0; rt < NT; ++rt) {
-      if (__builtin_expect(__any(lm[rt & 1] > thr(rt)), 0)) rescale(rt, lm[rt & 1]);
-      float bsum;
-      probs(s[rt & 1], rt, bsum);
-      lsum[rt] += bsum;
+      if (__builtin_expect(__any(lm[rt & 1] > thr[rt]), 0)) rescale(rt, lm[rt & 1]);
+      probs(s[rt & 1], rt);
       if (rt + 1 < NT) {
         qk(s[(rt + 1) & 1], rt + 1, H, valid, treeblk, hk, MASK_);
         lm[(rt + 1) & 1] = lane_max(s[(rt + 1) & 1]);
