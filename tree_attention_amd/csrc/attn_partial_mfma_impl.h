@@ -655,10 +655,12 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       convert(SN);
     }
     lds_barrier();
-    if (t + 3 < ntiles) dma(S, t + 3);
     // (after the last tile this reads a stage nobody uses; harmless, and it
     // keeps the P.V free of branches)
     pv(S, I1{}, [&] { kload(SN, I0{}); });
+    // stage S is free since the barrier; issued here rather than right after
+    // it, the loads no longer hold up the P.V products of every wave at once
+    if (t + 3 < ntiles) dma(S, t + 3);
   };
   if constexpr (BIGT) {
     if (tree) {  // the sequence's mask words to LDS, before any tile load is in flight
