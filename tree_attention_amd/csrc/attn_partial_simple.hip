@@ -111,17 +111,24 @@ __global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs 
 #pragma unroll
   for (int d = 0; d < D; ++d) acc[d] = 0.f;
 
-  // prefix keys (tiles 0 .. ptiles-1), then the tree keys (one more pass)
+  // prefix keys (tiles 0 .. ptiles-1), then the tree keys (one more pass).
+  // The elements of tile tt+1 are loaded into registers while tile tt is
+  // computed, so each tile's memory latency hides behind the one before.
   const int ptiles = (npk + kKeysPerTile - 1) / kKeysPerTile;
   const int ttiles = tree ? (a.T + kKeysPerTile - 1) / kKeysPerTile : 0;
-  for (int tt = 0; tt < ptiles + ttiles; ++tt) {
+  const int ntiles = ptiles + ttiles;
+  static_assert(kKeysPerTile * D % kThreadsWG == 0, "whole staging rounds");
+  constexpr int kPer = kKeysPerTile * D / kThreadsWG;  // elements per thread and tile
+  float kr[kPer], vr[kPer];
+  auto fetch = [&](int tt) {
     const bool intree = tt >= ptiles;
     const int t0 = (intree ? tt - ptiles : tt) * kKeysPerTile;
     const int n = min(kKeysPerTile, (intree ? a.T : npk) - t0);
     const Tin* kb = intree ? kt : kp;  // (a paged prefix tile addresses the pools itself)
     const Tin* vb = intree ? vt : vp;
-    __syncthreads();
-    for (int e = tid; e < kKeysPerTile * D; e += kThreadsWG) {
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int e = tid + it * kThreadsWG;
       const int j = e / D, d = e % D;
       const int key = t0 + min(j, n - 1);
       size_t off = key * kstride + d;
@@ -130,10 +137,24 @@ __global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs 
         kb = static_cast<const Tin*>(a.kp);
         vb = static_cast<const Tin*>(a.vp);
       }
-      ks[j][d] = to_f32(kb[off]);
-      vs[j][d] = to_f32(vb[off]);
+      kr[it] = to_f32(kb[off]);
+      vr[it] = to_f32(vb[off]);
+    }
+  };
+  if (ntiles > 0) fetch(0);
+  for (int tt = 0; tt < ntiles; ++tt) {
+    const bool intree = tt >= ptiles;
+    const int t0 = (intree ? tt - ptiles : tt) * kKeysPerTile;
+    const int n = min(kKeysPerTile, (intree ? a.T : npk) - t0);
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kPer; ++it) {
+      const int e = tid + it * kThreadsWG;
+      ks[e / D][e % D] = kr[it];
+      vs[e / D][e % D] = vr[it];
     }
     __syncthreads();
+    if (tt + 1 < ntiles) fetch(tt + 1);
     // tree keys t0 .. t0 + 31 lie in mask word t0 / 64
     const uint64_t mwt = (intree && active) ? mrow[t0 / 64] : 0ull;
     for (int j = sub; j < n; j += tpr) {
