@@ -16,8 +16,9 @@ MFMA peak, with its duration taken from HIP events recorded on the launch
 stream around replays of a graph of K launches of it on the same rotating
 inputs (median over the replays).  `us_per_call_spread` adds the median and
 minimum per call over further replays of the timed graph, and the same steps
-over a single KV copy that stays in the Infinity Cache (hot cache, labelled).  `cpu_baseline` times the fp64 oracle on a bounded sample of the same
-workload on the host cores.
+over a single KV copy that stays in the Infinity Cache (hot cache, labelled).
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same workload
+on the host cores.
 
 `--row NAME` measures one of the steps around the verification path instead
 (the draft's cross-attention into the target cache, its sliding-window
