@@ -227,20 +227,17 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   uint32_t vbits[NT];  // tree: this lane's mask bits (keys 8grp..8grp+7 of each block)
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
+    // a row past the workgroup's rows reads the last real row (without a
+    // branch per load): its results are never written
     const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
     const bool ok = r < x.rend;
-    const int i = ok ? r / a.G : 0;
-    const int hh = ok ? r % a.G : 0;
+    const int rr = ok ? r : x.rend - 1;
+    const int i = rr / a.G;
+    const int hh = rr % a.G;
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
                        ((static_cast<size_t>(x.b) * a.T + i) * a.Hq + x.g * a.G + hh) * D + grp * 8;
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c) {
-      if (ok) {
-        qf[rt][c] = *reinterpret_cast<const bf16x8*>(qp + c * 32);
-      } else {
-        qf[rt][c] = __builtin_bit_cast(bf16x8, (u32x4){0u, 0u, 0u, 0u});
-      }
-    }
+    for (int c = 0; c < C::DC; ++c) qf[rt][c] = *reinterpret_cast<const bf16x8*>(qp + c * 32);
     vbits[rt] = 0xffffu;
     if (!BIGT && (tree || head) && ok) {
       const uint64_t mw = a.mask[static_cast<size_t>(x.b) * a.T + i];
@@ -332,7 +329,7 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // slots of the raw V tile at this lane's position, so only this thread
   // reads them back.
   char* const sm = x.smem;
-  const bool vstage = tid < C::VTHREADS;
+  const bool vstage = C::VTHREADS == kThreads || tid < C::VTHREADS;  // compile-time true when every thread stages V
   // Loads go through buffer descriptors whose range ends with the tile's last
   // real key, so rows past it read as zeros (and are masked); per-thread byte
   // offsets within a tile:
