@@ -34,6 +34,7 @@ from .tree_attention_oracle import (  # noqa: F401
     ancestor_matrix,
     check_parent,
     gather_paged,
+    gather_strided,
     lse_merge,
     oracle_commit_kv,
     oracle_attn,

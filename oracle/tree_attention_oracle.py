@@ -69,6 +69,7 @@ __all__ = [
     "oracle_prefix_attn",
     "oracle_window_attn",
     "gather_paged",
+    "gather_strided",
     "oracle_commit_kv",
     "oracle_tree_rope",
     "round_bf16",
@@ -366,6 +367,35 @@ def gather_paged(pages, block_table, seq_lens, page_size):
     off[1:] = np.cumsum(lens)
     packed = np.stack(rows) if rows else np.zeros((0,) + pages.shape[2:], dtype=pages.dtype)
     return packed, off
+
+
+# --------------------------------------------------------------------------
+# Strided prefix cache
+# --------------------------------------------------------------------------
+
+def gather_strided(buf, offsets, row_stride, Hkv, D):
+    """The packed prefix layout of a cache whose key rows are not packed.
+
+    buf is a flat array; key j of sequence b, KV head g, feature d is
+    buf[(offsets[b] + j) * row_stride + g * D + d] (an interleaved K/V cache,
+    or rows padded past Hkv * D).  Returns packed [offsets[-1], Hkv, D], the
+    layout `oracle_attn` takes, so attention over a strided cache is attention
+    over the gathered rows.  Raises when a row reaches past the buffer or the
+    stride is shorter than a row.
+    """
+    flat = np.asarray(buf).reshape(-1)
+    off = np.asarray(offsets, dtype=np.int64)
+    rows = int(off[-1])
+    if row_stride < Hkv * D:
+        raise ValueError("row stride shorter than Hkv * D")
+    out = np.empty((rows, Hkv, D), dtype=flat.dtype)
+    for r in range(rows):
+        start = r * row_stride
+        if start + Hkv * D > flat.size:
+            raise ValueError(f"row {r} reaches past the buffer")
+        for g in range(Hkv):
+            out[r, g, :] = flat[start + g * D: start + g * D + D]
+    return out
 
 
 # --------------------------------------------------------------------------

@@ -492,6 +492,40 @@ def pin_gather_paged_contiguous_is_identity(orc):
         raise AssertionError("a page outside the pool was accepted")
 
 
+# ------------------------------------------------------------ strided cache
+
+def pin_gather_strided_hand_example(orc):
+    """Three rows of an interleaved cache [rows, 2, Hkv=1, D=2] worked by hand:
+    the buffer holds 0..11 in order, so K rows start at 0, 4, 8 and V rows at
+    2, 6, 10 (stride 4 = 2 * Hkv * D)."""
+    buf = np.arange(12, dtype=np.float64)
+    k = orc.gather_strided(buf, np.array([0, 2, 3]), 4, 1, 2)
+    v = orc.gather_strided(buf[2:], np.array([0, 2, 3]), 4, 1, 2)
+    assert k[:, 0, :].tolist() == [[0.0, 1.0], [4.0, 5.0], [8.0, 9.0]]
+    assert v[:, 0, :].tolist() == [[2.0, 3.0], [6.0, 7.0], [10.0, 11.0]]
+
+
+def pin_gather_strided_packed_is_identity(orc):
+    """Stride Hkv * D gives back the packed cache; padded rows (stride above
+    Hkv * D, padding filled with noise) give the same rows; a stride shorter
+    than a row is an error."""
+    rng = np.random.default_rng(67)
+    Hkv, D, lens = 3, 4, [5, 0, 2]
+    off = np.concatenate([[0], np.cumsum(lens)])
+    packed = rng.standard_normal((sum(lens), Hkv, D))
+    assert np.array_equal(orc.gather_strided(packed.reshape(-1), off, Hkv * D, Hkv, D), packed)
+    pad = 20
+    padded = rng.standard_normal((sum(lens), Hkv * D + pad))
+    padded[:, :Hkv * D] = packed.reshape(sum(lens), Hkv * D)
+    assert np.array_equal(orc.gather_strided(padded.reshape(-1), off, Hkv * D + pad, Hkv, D), packed)
+    try:
+        orc.gather_strided(packed.reshape(-1), off, Hkv * D - 1, Hkv, D)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a stride shorter than a row was accepted")
+
+
 # ------------------------------------------------------------ sliding window
 
 def _window_run(orc, w, window, **over):
