@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LTREE_VERSION 110 /* 1.1.0: paged caches, trees of up to 256 nodes, draft-side calls */
+#define LTREE_VERSION 120 /* 1.2.0: strided prefix caches */
 #define LTREE_MAX_TREE 256 /* largest tree; a mask row has W = ceil(T / 64) 64-bit words */
 #define LTREE_MAX_WINDOW (1 << 20) /* largest sliding window of ltree_window_attn */
 
@@ -139,9 +139,11 @@ size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
  *                  Its contents on entry do not matter.
  *
  * Numerics (bf16): q.k on bf16 MFMA with fp32 accumulation; softmax in fp32;
- * probabilities are rounded to fp16 and v converted exactly from bf16 to fp16
- * for the fp16 MFMA P.v product with fp32 accumulation; the row sums add the
- * same fp16-rounded probabilities.  Each split's normalised output row is
+ * probabilities are rounded to fp16 and v converted from bf16 to fp16 (round
+ * to nearest; exact for 2^-14 <= |v| < 65504, an absolute error of at most
+ * 2^-25 for smaller |v|, where fp16 is subnormal) for the fp16 MFMA P.v
+ * product with fp32 accumulation; the row sums add the same fp16-rounded
+ * probabilities.  Each split's normalised output row is
  * stored as 16-bit values relative to the row's largest magnitude (error at
  * most 2^-16 of it) for the merge.  |v| must stay below the fp16 limit 65504;
  * larger values give non-finite o.  fp32 path: fp32 throughout.
@@ -155,6 +157,47 @@ int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float sc
                const void* k_tree, const void* v_tree, const uint64_t* mask,
                float* o, float* lse, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
+
+/*
+ * ltree_attn_strided_workspace_bytes -- workspace size of ltree_attn_strided
+ * for these sizes and row strides on the current device (0 if invalid).
+ */
+size_t ltree_attn_strided_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
+                                          int max_prefix_len, int64_t k_row_stride,
+                                          int64_t v_row_stride);
+
+/*
+ * ltree_attn_strided -- ltree_attn over a prefix cache whose key rows are not
+ * packed: key j of sequence b, KV head g, feature d is
+ *
+ *     k_prefix[(prefix_offsets[b] + j) * k_row_stride + g * D + d]
+ *
+ * (likewise v_prefix with v_row_stride).  An interleaved cache [rows, 2, Hkv, D]
+ * is k_prefix = base, v_prefix = base + Hkv * D, both strides 2 * Hkv * D; a
+ * cache with padded rows has a stride above Hkv * D.  The computation is that
+ * of ltree_attn on the packed rows (gist.science section 2 part C); no copy
+ * is made.
+ *
+ *   k_row_stride, v_row_stride
+ *                  host, in elements: >= Hkv * D, a multiple of 8 (16-byte rows),
+ *                  at most 2^24.  LTREE_ERR_INVALID_ARG otherwise
+ *                  (LTREE_ERR_UNSUPPORTED above 2^24).
+ *   k_tree, v_tree, mask
+ *                  as for ltree_attn, packed [B, T, Hkv, D]; all three NULL
+ *                  computes the prefix part alone (as ltree_prefix_attn: an
+ *                  empty prefix gives o = 0 and lse = -inf).
+ *   workspace      >= ltree_attn_strided_workspace_bytes(...), 256-byte aligned.
+ *   other arguments as for ltree_attn.
+ *
+ * Returns as ltree_attn.  Two kernel launches.
+ */
+int ltree_attn_strided(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                       const void* q, const void* k_prefix, const void* v_prefix,
+                       int64_t k_row_stride, int64_t v_row_stride,
+                       const int32_t* prefix_offsets, int max_prefix_len,
+                       const void* k_tree, const void* v_tree, const uint64_t* mask,
+                       float* o, float* lse, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /*
  * ltree_attn_partials -- steps 1 and 2 of ltree_attn alone (same arguments
@@ -300,7 +343,10 @@ size_t ltree_window_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, in
  * window rule of ltree_window_attn, the cache addressed as in
  * ltree_attn_paged (k_pages, v_pages, num_pages, page_size, block_table,
  * max_pages_per_seq, seq_lens; only the last min(L_b, window - 1) keys of
- * each sequence are read, so only their pages need valid entries).  A window
+ * each sequence are read, so only their pages need valid entries).  A
+ * sequence with L_b above max_pages_per_seq * page_size (more keys than its
+ * block-table row can address) gets NaN in all its o and lse entries, and
+ * nothing of it is read, as for ltree_attn_paged.  A window
  * starts at any key, so rows are addressed lane by lane from the start of the
  * pool: num_pages * page_size * Hkv * D * element bytes must stay below 2^31
  * (else LTREE_ERR_UNSUPPORTED).  The workspace is

@@ -3,7 +3,8 @@ KV cache) on the GPU, through the C ABI, against the fp64 oracle.
 
 Small cases cover several key tiles and splits, ragged tails, an empty prefix
 (o = 0, lse = -inf), D = 64 and 128, bf16 and fp32.  The QwQ-shaped layer
-(prefix 32768, 64 query tokens) is checked on two KV heads' rows."""
+(prefix 32768, 64 query tokens) is checked on every row in
+test_gpu_full_sizes.py."""
 
 import zlib
 
@@ -13,7 +14,7 @@ import torch
 
 import oracle
 from gpu_helpers import BF16_O_TOL, F32_O_TOL, LSE_TOL, say
-from workloads import make_config, make_workload
+from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -67,36 +68,17 @@ def test_small_parity(name):
     _check(w, o, lse, o_ref, lse_ref)
 
 
-def test_many_splits(monkeypatch):
-    """64-key splits: 79 partials per row, more than a wavefront has lanes."""
-    monkeypatch.setenv("LTREE_SPLIT_KEYS", "64")
+def test_many_splits():
+    """One KV head over 20224 keys: 79 splits of 256 keys on a 256-CU device,
+    more partials per row than a wavefront has lanes."""
     rng = np.random.default_rng(5)
-    w = make_workload(rng, B=1, T=16, Hq=8, Hkv=2, D=128, prefix_lens=[5000], trees="chain",
+    w = make_workload(rng, B=1, T=16, Hq=8, Hkv=1, D=128, prefix_lens=[20224], trees="chain",
                       dtype="bf16", outlier_frac=0.01)
     say("prefix attn many splits")
     o, lse = _run(w)
     o_ref, lse_ref = oracle.oracle_prefix_attn(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(),
                                                w.scale)
     _check(w, o, lse, o_ref, lse_ref)
-
-
-def test_qwq_shape_two_kv_heads():
-    """The QwQ-shaped layer: prefix 32768, 64 query tokens, 40/8 heads, 1% of
-    prefix rows x8.  The oracle covers KV heads 0 and 5 (their 2 x 5 query
-    heads), a sub-problem of the same definition."""
-    w = make_config(4)
-    say("prefix attn qwq shape")
-    o, lse = _run(w)
-    G = 5
-    for g in (0, 5):
-        hs = slice(g * G, (g + 1) * G)
-        o_ref, lse_ref = oracle.oracle_prefix_attn(
-            w.q[:, :, hs], w.k_prefix[:, g:g + 1], w.v_prefix[:, g:g + 1], w.offsets.numpy(),
-            w.scale)
-        eo = np.max(np.abs(o[:, :, hs] - o_ref))
-        el = np.max(np.abs(lse[:, hs] - lse_ref))
-        assert eo <= BF16_O_TOL, f"kv head {g}: o max-abs error {eo:.3e}"
-        assert el <= LSE_TOL, f"kv head {g}: lse max-abs error {el:.3e}"
 
 
 def test_prefix_attn_equals_tree_attn_prefix_part():

@@ -5,7 +5,7 @@ Small cases cover windows shorter and longer than the cache, an empty cache,
 a window equal to T (the deepest node sees no cache key), windows that are
 not multiples of the 64-key tile, several splits, bf16 and fp32, D = 64 and
 128.  The QwQ-shaped case (window 512 after a 32768-row cache, 64 tree
-tokens, 40/8 heads) is checked on two KV heads' rows."""
+tokens, 40/8 heads) is checked on every row in test_gpu_full_sizes.py."""
 
 import zlib
 
@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from gpu_helpers import BF16_O_TOL, F32_O_TOL, LSE_TOL, say
-from workloads import make_config, make_workload
+from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -90,17 +90,18 @@ def test_small_parity(name):
     _check(w, o, lse, o_ref, lse_ref)
 
 
-@pytest.mark.parametrize("split", [64, 192])
-def test_split_sizes(monkeypatch, split):
-    """Splits of one tile and of three tiles (the first of which is the
-    window's per-row masked head tile)."""
-    monkeypatch.setenv("LTREE_SPLIT_KEYS", str(split))
-    rng = np.random.default_rng(split)
-    w = make_workload(rng, B=2, T=64, Hq=8, Hkv=2, D=128, prefix_lens=[2000, 400],
+@pytest.mark.parametrize("window,lens", [(512, [2000, 400]), (20000, [20000, 400])])
+def test_split_sizes(window, lens):
+    """Splits of one tile (window 512: 511 keys over 128 splits per head,
+    rounded up to 64) and of three tiles (window 20000: 19999 keys, 192-key
+    splits), on a 256-CU device; the first split is the window's per-row
+    masked head tile."""
+    rng = np.random.default_rng(window)
+    w = make_workload(rng, B=2, T=64, Hq=8, Hkv=2, D=128, prefix_lens=lens,
                       trees=("bounded", 8, 3), dtype="bf16", outlier_frac=0.01)
-    say("window attn split", split)
-    o, lse = _run(w, 512)
-    o_ref, lse_ref = _reference(w, 512)
+    say("window attn split", window)
+    o, lse = _run(w, window)
+    o_ref, lse_ref = _reference(w, window)
     _check(w, o, lse, o_ref, lse_ref)
 
 
@@ -117,19 +118,6 @@ def test_window_covering_everything_equals_tree_attention():
     torch.cuda.synchronize()
     assert np.max(np.abs(o - o2.cpu().double().numpy())) <= BF16_O_TOL
     assert np.max(np.abs(lse - lse2.cpu().double().numpy())) <= LSE_TOL
-
-
-def test_qwq_shape_two_kv_heads():
-    """Window 512 over the QwQ-shaped layer's 32768-row cache (only the last
-    511 rows are read), 64 tree tokens, 40/8 heads; KV heads 0 and 5."""
-    w = make_config(4)
-    say("window attn qwq shape")
-    o, lse = _run(w, 512)
-    for hs, (o_ref, lse_ref) in _reference(w, 512, heads=(0, 5)):
-        eo = np.max(np.abs(o[:, :, hs] - o_ref))
-        el = np.max(np.abs(lse[:, hs] - lse_ref))
-        assert eo <= BF16_O_TOL, f"o max-abs error {eo:.3e}"
-        assert el <= LSE_TOL, f"lse max-abs error {el:.3e}"
 
 
 def test_window_shorter_than_tree_is_rejected():
@@ -182,3 +170,40 @@ def test_window_over_paged_cache(P, name):
     o_ref, lse_ref = oracle.oracle_window_attn(w.q, kg, vg, off, w.k_tree, w.v_tree,
                                                w.parent.numpy(), w.scale, window)
     _check(w, o, lse, o_ref, lse_ref)
+
+
+def test_window_paged_sequence_past_block_table_gives_nan():
+    """A sequence with more keys than its block-table row reaches (L_b above
+    max_pages_per_seq * page_size) gets NaN rows and none of its pages is
+    looked up; the other sequences stay exact.  The last sequence is the one
+    past its row, so a lookup would have gone past the end of the table."""
+    import tree_attention_amd as ta
+    from test_gpu_paged import _paginate
+    w, window = _case("w200_ragged_empty")            # lens [700, 0, 150], window 200
+    P = 16
+    rng = np.random.default_rng(5)
+    kp, vp, bt, lens = _paginate(w, P, rng)
+    reach = bt.shape[1] * P                           # 44 pages of 16 keys: 704
+    lens_bad = lens.clone()
+    lens_bad[2] = reach + 1
+    dev = "cuda"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_tree.shape[2]
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty((ta.ltree_window_attn_paged_workspace_bytes(B, T, Hq, Hkv, D, window, P),),
+                     dtype=torch.uint8, device=dev)
+    say("window paged past the block table")
+    assert ta.ltree_window_attn_paged(w.q.to(dev), kp.to(dev), vp.to(dev), bt.to(dev),
+                                      lens_bad.to(dev), w.k_tree.to(dev), w.v_tree.to(dev), mask,
+                                      o, lse, ws, w.scale, window) == 0
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.all(np.isnan(o[2])) and np.all(np.isnan(lse[2]))
+    kg, off = oracle.gather_paged(kp.float().numpy(), bt.numpy(), lens.numpy(), P)
+    vg, _ = oracle.gather_paged(vp.float().numpy(), bt.numpy(), lens.numpy(), P)
+    o_ref, lse_ref = oracle.oracle_window_attn(w.q, kg, vg, off, w.k_tree, w.v_tree,
+                                               w.parent.numpy(), w.scale, window)
+    assert np.max(np.abs(o[:2] - o_ref[:2])) <= BF16_O_TOL
+    assert np.max(np.abs(lse[:2] - lse_ref[:2])) <= LSE_TOL

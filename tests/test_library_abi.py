@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
               "ltree_version", "ltree_prefix_attn", "ltree_window_attn",
               "ltree_window_attn_workspace_bytes", "ltree_attn_paged",
               "ltree_attn_paged_workspace_bytes", "ltree_window_attn_paged",
-              "ltree_window_attn_paged_workspace_bytes", "ltree_tree_rope", "ltree_commit_kv"):
+              "ltree_window_attn_paged_workspace_bytes", "ltree_tree_rope", "ltree_commit_kv",
+              "ltree_attn_strided", "ltree_attn_strided_workspace_bytes"):
         assert n in names
 
 
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     import tree_attention_amd as ta
-    assert ta.ltree_version() == 110
+    assert ta.ltree_version() == 120
     assert ta.ltree_status_string(0) == "ok"
     assert "workspace" in ta.ltree_status_string(ta.LTREE_ERR_WORKSPACE)
     assert ta.ltree_status_string(12345) == "unknown status"
@@ -103,3 +104,28 @@ def test_build_mask_argument_errors():
     assert fn(0x1000, 1, 8, None, None, None) == -1
     assert fn(0x1000, 0, 8, 0x2000, None, None) == -1
     assert fn(0x1000, 1, 257, 0x2000, None, None) == -2
+
+
+def test_strided_workspace_sizing():
+    import tree_attention_amd as ta
+    packed = ta.ltree_attn_workspace_bytes(1, 64, 40, 8, 128, 32768)
+    # an interleaved cache (stride 2 * Hkv * D) plans like the packed one
+    assert ta.ltree_attn_strided_workspace_bytes(1, 64, 40, 8, 128, 32768, 2048, 2048) == packed
+    for ks, vs in [(1023, 1024), (1024, 1000), (1028, 1024), (0, 1024), (1 << 25, 1024)]:
+        assert ta.ltree_attn_strided_workspace_bytes(1, 64, 40, 8, 128, 32768, ks, vs) == 0, (ks, vs)
+
+
+@no_gpu
+@pytest.mark.parametrize("ks,vs,expect", [
+    (1024, 1024, -3), (2048, 1024, -3),        # valid strides: stopped by the tiny workspace
+    (1023, 1024, -1), (1024, 1020, -1), (1032 + 4, 1024, -1), (1 << 25, 1024, -2),
+])
+def test_strided_argument_errors(ks, vs, expect):
+    lib, ta = _raw()
+    fn = lib.ltree_attn_strided
+    P, I, S, F, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float, ctypes.c_int64
+    fn.restype = I
+    fn.argtypes = [I, I, I, I, I, I, F, P, P, P, L, L, P, I, P, P, P, P, P, P, S, P]
+    st = fn(1, 1, 8, 8, 8, 128, 0.1, 0x1000, 0x2000, 0x3000, ks, vs, 0x4000, 100, 0x5000,
+            0x6000, 0x7000, 0x8000, 0x9000, 0x100000, 16, None)
+    assert st == expect

@@ -19,12 +19,15 @@ from ._binding import (  # noqa: F401
     LTreeError,
     attn,
     attn_paged,
+    attn_strided,
     build_mask,
     ltree_attn,
     ltree_attn_merge,
     ltree_attn_paged,
     ltree_attn_paged_workspace_bytes,
     ltree_attn_partials,
+    ltree_attn_strided,
+    ltree_attn_strided_workspace_bytes,
     ltree_attn_workspace_bytes,
     ltree_build_mask,
     ltree_commit_kv,

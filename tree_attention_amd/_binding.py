@@ -30,7 +30,8 @@ LTREE_MAX_TREE = 256
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
             "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
-            "ltree_attn_merge", "ltree_prefix_attn", "ltree_attn_paged_workspace_bytes",
+            "ltree_attn_merge", "ltree_prefix_attn", "ltree_attn_strided_workspace_bytes",
+            "ltree_attn_strided", "ltree_attn_paged_workspace_bytes",
             "ltree_attn_paged", "ltree_window_attn_paged_workspace_bytes",
             "ltree_window_attn_paged", "ltree_window_attn_workspace_bytes",
             "ltree_window_attn", "ltree_commit_kv", "ltree_tree_rope")
@@ -49,6 +50,7 @@ def _load() -> ctypes.CDLL:
             "(hipcc, gfx950) first")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I, S, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
+    L = ctypes.c_int64
     sig = {
         "ltree_version": (I, []),
         "ltree_status_string": (ctypes.c_char_p, [I]),
@@ -58,6 +60,9 @@ def _load() -> ctypes.CDLL:
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
         "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
+        "ltree_attn_strided_workspace_bytes": (S, [I, I, I, I, I, I, L, L]),
+        "ltree_attn_strided": (I, [I, I, I, I, I, I, F, P, P, P, L, L, P, I, P, P, P, P, P, P,
+                                   S, P]),
         "ltree_attn_paged_workspace_bytes": (S, [I, I, I, I, I, I, I]),
         "ltree_attn_paged": (I, [I, I, I, I, I, I, F, P, P, P, I, I, P, I, P, I, P, P, P, P, P, P,
                                  S, P]),
@@ -237,6 +242,60 @@ def ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, 
     return _lib.ltree_prefix_attn(
         _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
         _ptr(prefix_offsets), int(max_prefix_len), _ptr(o), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+
+
+def _row_view(t, name, Hkv, D, dtype):
+    """A [rows, Hkv, D] device view whose (Hkv, D) part is packed; returns its
+    row stride in elements."""
+    if t is None or not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 3 or t.shape[1:] != (Hkv, D) or t.stride(2) != 1 or t.stride(1) != D:
+        raise ValueError(f"{name} must be a [rows, Hkv, D] view with packed (Hkv, D)")
+    return t.stride(0) if t.shape[0] > 1 else Hkv * D
+
+
+def ltree_attn_strided_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len, k_row_stride,
+                                       v_row_stride) -> int:
+    return int(_lib.ltree_attn_strided_workspace_bytes(B, T, Hq, Hkv, D, int(max_prefix_len),
+                                                       int(k_row_stride), int(v_row_stride)))
+
+
+def ltree_attn_strided(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree,
+                       mask, o, lse, workspace, scale, stream=None) -> int:
+    """ltree_attn over prefix views [rows, Hkv, D] whose rows are `stride(0)`
+    elements apart (e.g. kv[:, 0] and kv[:, 1] of an interleaved cache
+    [rows, 2, Hkv, D]).  k_tree, v_tree and mask all None: prefix only."""
+    dt = q.dtype
+    _dev(q, "q", dt)
+    B, T, Hq, D = q.shape
+    has_tree = k_tree is not None
+    if has_tree:
+        _dev(k_tree, "k_tree", dt)
+        _dev(v_tree, "v_tree", dt)
+        _dev(mask, "mask", torch.int64)
+        Hkv = k_tree.shape[2]
+        if k_tree.shape != (B, T, Hkv, D) or v_tree.shape != (B, T, Hkv, D):
+            raise ValueError("k_tree/v_tree must be [B, T, Hkv, D]")
+        _check_mask(mask, B, T)
+    else:
+        Hkv = k_prefix.shape[1]
+    ks = _row_view(k_prefix, "k_prefix", Hkv, D, dt)
+    vs = _row_view(v_prefix, "v_prefix", Hkv, D, dt)
+    _dev(prefix_offsets, "prefix_offsets", torch.int32)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    _dev(workspace, "workspace")
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    return _lib.ltree_attn_strided(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp), int(ks),
+        int(vs), _ptr(prefix_offsets), int(max_prefix_len), _ptr(k_tree), _ptr(v_tree),
+        _ptr(mask), _ptr(o), _ptr(lse), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(stream))
 
 
@@ -440,6 +499,27 @@ def prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, scale, wo
                            workspace, scale, stream)
     if st != LTREE_OK:
         raise LTreeError(st, "ltree_prefix_attn")
+    return o, lse
+
+
+def attn_strided(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree, mask,
+                 scale, workspace=None, stream=None):
+    """Allocate o and lse (and the workspace) and run ltree_attn_strided."""
+    B, T, Hq, D = q.shape
+    Hkv = k_prefix.shape[1]
+    o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, T), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        ks = _row_view(k_prefix, "k_prefix", Hkv, D, q.dtype)
+        vs = _row_view(v_prefix, "v_prefix", Hkv, D, q.dtype)
+        n = ltree_attn_strided_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len, ks, vs)
+        if n == 0:
+            raise LTreeError(LTREE_ERR_INVALID_ARG, "ltree_attn_strided_workspace_bytes")
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    st = ltree_attn_strided(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree,
+                            v_tree, mask, o, lse, workspace, scale, stream)
+    if st != LTREE_OK:
+        raise LTreeError(st, "ltree_attn_strided")
     return o, lse
 
 

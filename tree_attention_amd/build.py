@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libltree.so")
 
-SOURCES = ["ltree_api.hip", "mask_build.hip", "attn_partial_mfma.hip",
-           "attn_partial_mfma_window.hip", "attn_partial_mfma_paged.hip",
+SOURCES = ["ltree_api.hip", "ltree_plan.cpp", "mask_build.hip", "attn_partial_mfma.hip",
+           "attn_partial_mfma_window.hip", "attn_partial_mfma_paged.hip", "attn_partial_mfma_strided.hip",
            "attn_partial_simple.hip", "lse_merge.hip", "kv_commit.hip",
            "tree_rope.hip"]
 
@@ -36,7 +36,7 @@ HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # every float max can be dropped there.
 EXTRA_FLAGS = {name: ["-fno-honor-nans"] for name in
                ("attn_partial_mfma.hip", "attn_partial_mfma_window.hip",
-                "attn_partial_mfma_paged.hip")}
+                "attn_partial_mfma_paged.hip", "attn_partial_mfma_strided.hip")}
 
 
 def hipcc() -> str:
@@ -52,7 +52,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     from concurrent.futures import ThreadPoolExecutor
 
     def compile_one(src):
-        obj = os.path.join(CSRC, "_obj", src.replace(".hip", ".o"))
+        obj = os.path.join(CSRC, "_obj", os.path.splitext(src)[0] + ".o")
         os.makedirs(os.path.dirname(obj), exist_ok=True)
         cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]

@@ -32,6 +32,9 @@ hipError_t launch_partials_mfma(const Plan& p, PartialArgs a, hipStream_t stream
   const bool paged = a.block_table != nullptr;
   const bool lane_paged = paged && (a.window > 0 || a.page_size % kTile != 0);
   if (a.window > 0) return launch_mfma_window(big, lane_paged, p.D, tpw, grid, a, stream);
+  if (a.kstride != a.Hkv * p.D || a.vstride != a.Hkv * p.D) {
+    return launch_mfma_strided(big, p.D, tpw, grid, a, stream);
+  }
   if (paged) return launch_mfma_paged(big, lane_paged, p.D, tpw, grid, a, stream);
   return launch_mfma_plain(big, p.D, tpw, grid, a, stream);
 }

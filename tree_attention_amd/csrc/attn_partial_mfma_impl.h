@@ -189,7 +189,9 @@ struct Ctx {
   const __bf16* vbase;
   const __bf16* ktree;  // tree key 0 of this sequence, KV head g
   const __bf16* vtree;
-  int kstride;          // elements between consecutive keys
+  int kstride;          // elements between consecutive prefix keys: K (the packed pool when paged)
+  int vstride;          // ... of V
+  int tstride;          // ... of the tree keys (Hkv * D)
   int kfirst;           // key index (within the sequence) of this partial's first prefix key
   int npk;              // prefix keys of this partial
   bool tree;            // the tree keys follow them
@@ -207,12 +209,13 @@ struct Ctx {
 // BIGT: trees of more than 64 nodes: ceil(T/64) tree tiles, whose mask bits
 // each row tile reads from a copy of the sequence's mask words in LDS at the
 // start of the tile (W = ceil(T/64) words per row).
+// STR: prefix K and V rows at the caller's strides (tree rows packed).
 // PAGED: the prefix keys live in pages of a shared pool; the page numbers of
 // the split are copied to LDS first.  PAGED == 1 (page size a multiple of
 // 64): each 64-key tile lies in one page and gets its own base.  PAGED == 2
 // (any page size, a pool below 4 GB): one buffer spans the pool and every
 // lane finds its own row's page.
-template <int D, int NT, bool WIN, bool BIGT, int PAGED>
+template <int D, int NT, bool WIN, bool BIGT, int PAGED, bool STR>
 __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
@@ -296,7 +299,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   // prefix tiles, then the tree tiles (one for T <= 64)
   const int ptiles = (npk + kTile - 1) / kTile;
   const int ntiles = ptiles + (tree ? (BIGT ? (T + kTile - 1) / kTile : 1) : 0);
+  // STR: a strided prefix cache (other row strides than the packed tree);
+  // otherwise one stride serves every tile
   const int kstride = x.kstride;
+  const int vstride = STR ? x.vstride : kstride;
+  const int tstride = STR ? x.tstride : kstride;
 
   // ---- per-lane LDS offsets of the MFMA operands.  Stage, block half, sub
   // block, d tile and V^T buffer are compile-time and go into the 16-bit
@@ -343,8 +350,8 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
 #pragma unroll
   for (int i = 0; i < C::VIPT; ++i) {
     const int it = tid + i * kThreads, vm = it / C::KC16, vc = it % C::KC16;
-    vsoff[i][0] = ((2 * vm) * kstride + vc * 8) * 2;
-    vsoff[i][1] = vsoff[i][0] + kstride * 2;
+    vsoff[i][0] = ((2 * vm) * vstride + vc * 8) * 2;
+    vsoff[i][1] = vsoff[i][0] + vstride * 2;
   }
   // PAGED: the split's page numbers in LDS (after the mask words, if any)
   const int32_t* pst = reinterpret_cast<const int32_t*>(sm + C::SMEM + (BIGT ? kMaskStash : 0));
@@ -362,11 +369,13 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
     const bool tt = BIGT ? t >= ptiles : t == ptiles;  // a tree tile
     const int u = BIGT ? t - ptiles : 0;                // its index among the tree tiles
     const int nrows = tt ? (BIGT ? min(kTile, T - u * kTile) : T) : min(kTile, npk - t * kTile);
-    const size_t toff = tt ? (BIGT ? static_cast<size_t>(u) * kTile * kstride : 0)
-                           : static_cast<size_t>(t) * kTile * kstride;
-    const int bytes = nrows * kstride * 2;
-    const __bf16* kb = (tt ? x.ktree : x.kbase) + toff;
-    const __bf16* vb = (tt ? x.vtree : x.vbase) + toff;
+    // first row of the tile; row strides: the caller's for prefix tiles, the
+    // packed tree layout for tree tiles
+    const size_t trow = tt ? (BIGT ? static_cast<size_t>(u) * kTile : 0) : static_cast<size_t>(t) * kTile;
+    const int ks = tt ? tstride : kstride;
+    const int vs = tt ? tstride : vstride;
+    const __bf16* kb = (tt ? x.ktree : x.kbase) + trow * ks;
+    const __bf16* vb = (tt ? x.vtree : x.vbase) + trow * vs;
     if constexpr (PAGED == 2) {
       if (!tt) {  // one buffer over the pool (from KV head g on); rows by lane below
         kb = static_cast<const __bf16*>(a.kp) + x.g * D;
@@ -385,13 +394,22 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
       }
     }
     const bool lane_rows = PAGED == 2 && !tt;
-    const int range = lane_rows ? static_cast<int>(a.pool_bytes - static_cast<uint32_t>(x.g * D * 2)) : bytes;
-    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kb), 0, range, kBufferFlags);
-    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vb), 0, range, kBufferFlags);
+    const int pool_range = static_cast<int>(a.pool_bytes - static_cast<uint32_t>(x.g * D * 2));
+    const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(kb), 0,
+                                                      lane_rows ? pool_range : nrows * ks * 2, kBufferFlags);
+    const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(vb), 0,
+                                                      lane_rows ? pool_range : nrows * vs * 2, kBufferFlags);
+    // a strided prefix with other strides than the tree: the tree tile's
+    // per-thread offsets at the tree stride
+    const bool restride = STR && tt && (kstride != tstride || vstride != tstride);
 #pragma unroll
     for (int j = 0; j < C::KDMA; ++j) {
       char* dst = sm + Cfg<D>::K0 + S * Cfg<D>::BUF + (j * kWaves + wave) * 1024;
       int vo = ksoff[j];
+      if (restride) {
+        const int row = (j * kWaves + wave) * C::ROWS_PER_DMA + lane / C::KC16;
+        vo = (row * tstride + (((lane % C::KC16) ^ kswz<D>(row)) * 8)) * 2;
+      }
       if constexpr (PAGED == 2) {
         if (lane_rows) {  // rows past the tile's last key repeat it (they are masked)
           const int row = (j * kWaves + wave) * C::ROWS_PER_DMA + lane / C::KC16;
@@ -410,6 +428,10 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
           char* dst = sm + Cfg<D>::R0 + S * Cfg<D>::BUF +
                       (j * (Cfg<D>::VITEMS / 64) + i * kWaves + wave) * 1024;
           int vo = vsoff[i][j];
+          if (restride) {
+            const int it = tid + i * kThreads, vm = it / C::KC16, vc = it % C::KC16;
+            vo = ((2 * vm + j) * tstride + vc * 8) * 2;
+          }
           if constexpr (PAGED == 2) {
             if (lane_rows) {
               const int it = tid + i * kThreads, vm = it / C::KC16, vc = it % C::KC16;
@@ -763,10 +785,11 @@ __device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
   }
 }
 
-template <int D, int TPW, bool WIN, bool BIGT, int PAGED>
+template <int D, int TPW, bool WIN, bool BIGT, int PAGED, bool STR>
 __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a) {
   using C = Cfg<D>;
   static_assert(!(WIN && PAGED == 1), "a window starts anywhere: rows by lane over a paged cache");
+  static_assert(!(STR && (WIN || PAGED)), "strided rows only for the packed-cache verification variant");
   __shared__ __attribute__((aligned(1024)))
   char smem[C::SMEM + (BIGT ? kMaskStash : 0) + (PAGED ? kPageStash : 0)];
 
@@ -786,7 +809,7 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   const int off0 = PAGED ? 0 : a.offsets[x.b];
   const int L = PAGED ? a.seq_lens[x.b] : a.offsets[x.b + 1] - off0;
   int start, n;
-  if (!key_range(L, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
+  if (!key_range(L, a.window, a.max_prefix_len, a.seq_cap, &start, &n)) return;  // the merge reports it
   // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
   // (slot 0 when n = 0) also the tree keys
   const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
@@ -801,10 +824,13 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.head = a.window > 0 && x.npk > 0 && k0 < kHeadKeys;
   x.hbase = n - a.window;
   x.hk0 = k0;
-  x.kstride = a.Hkv * D;
+  // prefix rows at the caller's strides (a paged pool is packed: Hkv * D)
+  x.tstride = a.Hkv * D;
+  x.kstride = PAGED ? x.tstride : a.kstride;
+  x.vstride = PAGED ? x.tstride : a.vstride;
   const size_t row0 = static_cast<size_t>(off0) + start + k0;
-  x.kbase = static_cast<const __bf16*>(a.kp) + (row0 * a.Hkv + x.g) * D;
-  x.vbase = static_cast<const __bf16*>(a.vp) + (row0 * a.Hkv + x.g) * D;
+  x.kbase = static_cast<const __bf16*>(a.kp) + row0 * x.kstride + x.g * D;
+  x.vbase = static_cast<const __bf16*>(a.vp) + row0 * x.vstride + x.g * D;
   x.ktree = static_cast<const __bf16*>(a.kt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
   x.vtree = static_cast<const __bf16*>(a.vt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
   if (x.npk == 0) {  // tree only: the prefix pointers may not be dereferenceable
@@ -820,33 +846,33 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   const int ntw = (tiles - x.wave + kWaves - 1) / kWaves;  // tiles wave, wave+8, ... < tiles
   if constexpr (TPW >= 3) {
     if (ntw >= 3) {
-      run<D, 3, WIN, BIGT, PAGED>(x);
+      run<D, 3, WIN, BIGT, PAGED, STR>(x);
       return;
     }
   }
   if constexpr (TPW >= 2) {
     if (ntw == 2) {
-      run<D, 2, WIN, BIGT, PAGED>(x);
+      run<D, 2, WIN, BIGT, PAGED, STR>(x);
       return;
     }
   }
-  run<D, 1, WIN, BIGT, PAGED>(x);  // one tile, or none: a wave without rows still stages and syncs
+  run<D, 1, WIN, BIGT, PAGED, STR>(x);  // one tile, or none: a wave without rows still stages and syncs
 }
 
-template <int D, bool WIN, bool BIGT, int PAGED>
+template <int D, bool WIN, bool BIGT, int PAGED, bool STR>
 hipError_t launch_d(int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
   switch (tpw) {
-    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
-    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN, BIGT, PAGED>), grid, dim3(kThreads), 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((partial_mfma_kernel<D, 1, WIN, BIGT, PAGED, STR>), grid, dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((partial_mfma_kernel<D, 2, WIN, BIGT, PAGED, STR>), grid, dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((partial_mfma_kernel<D, 3, WIN, BIGT, PAGED, STR>), grid, dim3(kThreads), 0, stream, a); break;
   }
   return hipGetLastError();
 }
 
-template <bool WIN, bool BIGT, int PAGED>
+template <bool WIN, bool BIGT, int PAGED, bool STR = false>
 hipError_t launch_dd(int D, int tpw, dim3 grid, PartialArgs a, hipStream_t stream) {
-  return D == 128 ? launch_d<128, WIN, BIGT, PAGED>(tpw, grid, a, stream)
-                  : launch_d<64, WIN, BIGT, PAGED>(tpw, grid, a, stream);
+  return D == 128 ? launch_d<128, WIN, BIGT, PAGED, STR>(tpw, grid, a, stream)
+                  : launch_d<64, WIN, BIGT, PAGED, STR>(tpw, grid, a, stream);
 }
 
 }  // namespace
@@ -854,6 +880,7 @@ hipError_t launch_dd(int D, int tpw, dim3 grid, PartialArgs a, hipStream_t strea
 // Launchers of the variants, one translation unit per group (external
 // linkage; the kernels themselves stay local to their unit).
 hipError_t launch_mfma_plain(bool big, int D, int tpw, dim3 grid, PartialArgs a, hipStream_t s);
+hipError_t launch_mfma_strided(bool big, int D, int tpw, dim3 grid, PartialArgs a, hipStream_t s);
 hipError_t launch_mfma_window(bool big, bool lane_paged, int D, int tpw, dim3 grid, PartialArgs a,
                               hipStream_t s);
 hipError_t launch_mfma_paged(bool big, bool lane_paged, int D, int tpw, dim3 grid, PartialArgs a,

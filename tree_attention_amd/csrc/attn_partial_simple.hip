@@ -52,7 +52,7 @@ __global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs 
   const int off0 = paged ? 0 : a.offsets[b];
   const int L = paged ? a.seq_lens[b] : a.offsets[b + 1] - off0;
   int start, n;
-  if (!key_range(L, a.window, a.max_prefix_len, &start, &n)) return;  // the merge reports it
+  if (!key_range(L, a.window, a.max_prefix_len, a.seq_cap, &start, &n)) return;  // the merge reports it
   // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
   // (slot 0 when n = 0) also the tree keys
   const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
@@ -60,10 +60,13 @@ __global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs 
   const int k0 = slot * a.chunk;
   const int npk = max(0, min(a.chunk, n - k0));
   const bool tree = a.has_tree && slot == nparts - 1;
-  const size_t kstride = static_cast<size_t>(a.Hkv) * D;
+  // prefix rows at the caller's strides (a paged pool, and the tree, are packed)
+  const size_t tstride = static_cast<size_t>(a.Hkv) * D;
+  const size_t kstr = paged ? tstride : static_cast<size_t>(a.kstride);
+  const size_t vstr = paged ? tstride : static_cast<size_t>(a.vstride);
   const size_t row0 = static_cast<size_t>(off0) + start + k0;
-  const Tin* kp = static_cast<const Tin*>(a.kp) + (row0 * a.Hkv + g) * D;
-  const Tin* vp = static_cast<const Tin*>(a.vp) + (row0 * a.Hkv + g) * D;
+  const Tin* kp = static_cast<const Tin*>(a.kp) + row0 * kstr + static_cast<size_t>(g) * D;
+  const Tin* vp = static_cast<const Tin*>(a.vp) + row0 * vstr + static_cast<size_t>(g) * D;
   const Tin* kt = static_cast<const Tin*>(a.kt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
   const Tin* vt = static_cast<const Tin*>(a.vt) + (static_cast<size_t>(b) * a.T * a.Hkv + g) * D;
 
@@ -131,14 +134,15 @@ __global__ __launch_bounds__(kThreadsWG) void partial_simple_kernel(PartialArgs 
       const int e = tid + it * kThreadsWG;
       const int j = e / D, d = e % D;
       const int key = t0 + min(j, n - 1);
-      size_t off = key * kstride + d;
+      size_t koff = key * (intree ? tstride : kstr) + d;
+      size_t voff = key * (intree ? tstride : vstr) + d;
       if (paged && !intree) {
-        off = page_row(start + k0 + key) * kstride + static_cast<size_t>(g) * D + d;
+        koff = voff = page_row(start + k0 + key) * tstride + static_cast<size_t>(g) * D + d;
         kb = static_cast<const Tin*>(a.kp);
         vb = static_cast<const Tin*>(a.vp);
       }
-      kr[it] = to_f32(kb[off]);
-      vr[it] = to_f32(vb[off]);
+      kr[it] = to_f32(kb[koff]);
+      vr[it] = to_f32(vb[voff]);
     }
   };
   if (ntiles > 0) fetch(0);

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     const void* __restrict__ o_part,
     const float* __restrict__ scale_part, const float* __restrict__ lse_part,
     float* __restrict__ o, float* __restrict__ lse, int B, int T, int Hq, int Hkv, int G, int R,
-    int chunk, int slots, int max_prefix_len, int window) {
+    int chunk, int slots, int max_prefix_len, int window, int seq_cap) {
   constexpr int FPL = D / 64;  // features per lane
   const int j = threadIdx.x & 63;
   // rows are ordered (b, h, i) so the lse writes [B, Hq, T] are contiguous;
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   int start, n;
   const int L = seq_lens != nullptr ? seq_lens[b] : offsets[b + 1] - offsets[b];
   const float nan = __builtin_nanf("");
-  if (!key_range(L, window, max_prefix_len, &start, &n)) {
+  if (!key_range(L, window, max_prefix_len, seq_cap, &start, &n)) {
     // The prefix-length table disagrees with max_prefix_len: fail loudly.
 #pragma unroll
     for (int f = 0; f < FPL; ++f) orow[f] = nan;
@@ -182,7 +182,7 @@ void launch_typed(const Plan& p, dim3 grid, const int32_t* offsets, const int32_
                   hipStream_t stream) {
   hipLaunchKernelGGL((lse_merge_kernel<D, SNORM>), grid, dim3(64 * kMergeWaves), 0, stream,
                      offsets, seq_lens, o_part, scale_part, lse_part, o, lse, p.B, p.T, p.Hq, p.Hkv, p.G,
-                     p.R, p.chunk, p.slots, p.max_prefix_len, p.window);
+                     p.R, p.chunk, p.slots, p.max_prefix_len, p.window, p.seq_cap);
 }
 
 }  // namespace

@@ -2,7 +2,6 @@
 // The operations are defined in include/ltree.h.
 #include <atomic>
 #include <cmath>
-#include <cstdlib>
 
 #include "ltree_internal.h"
 
@@ -11,8 +10,6 @@ namespace ltree {
 namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
-
-inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 }  // namespace
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -30,67 +27,18 @@ int device_cu_count() {
   return n;
 }
 
-bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window,
-               int page_size) {
-  if (page_size < 0) return false;
-  if (window < 0 || window > LTREE_MAX_WINDOW || (window > 0 && window < T)) return false;
-  if (window > 0) max_prefix_len = window - 1;
-  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) return false;
-  if (D != 64 && D != 128) return false;
-  if (T > LTREE_MAX_TREE) return false;
-  // output rows (b, h, i) are indexed with 32-bit integers in the merge
-  if (static_cast<long>(B) * Hq * T >= (1L << 31)) return false;
-  p->B = B;
-  p->T = T;
-  p->Hq = Hq;
-  p->Hkv = Hkv;
-  p->D = D;
-  p->G = Hq / Hkv;
-  p->R = p->G * T;
-  p->max_prefix_len = max_prefix_len;
-  p->window = window;
-
-  // Split size: enough prefix splits per KV head that the Hkv heads of one
-  // sequence cover every compute unit once; never below 256 keys, so that a
-  // split's partial output stays small next to the keys it reads (a window of
-  // a few hundred keys, whose call is latency-bound, splits down to 64).
-  const int cus = device_cu_count();
-  const int per_head = (cus + Hkv - 1) / Hkv;
-  long chunk = (static_cast<long>(max_prefix_len) + per_head - 1) / per_head;
-  chunk = (chunk + 63) / 64 * 64;
-  const long min_chunk = window > 0 ? 64 : 256;
-  if (chunk < min_chunk) chunk = min_chunk;
-  if (const char* env = std::getenv("LTREE_SPLIT_KEYS")) {  // tuning sweeps only
-    const long v = std::atol(env);
-    if (v >= 64 && v % 64 == 0) chunk = v;
-  }
-  // keys of one split are addressed with 32-bit element offsets
-  const long cap = ((1L << 31) - 1) / (static_cast<long>(Hkv) * D) / 64 * 64;
-  if (chunk > cap) chunk = cap;
-  // a paged split's page numbers fit the kernels' LDS table (a split that
-  // starts inside a page touches one page more than it fills)
-  if (page_size > 0 && chunk > static_cast<long>(kMaxSplitPages - 1) * page_size) {
-    chunk = static_cast<long>(kMaxSplitPages - 1) * page_size / 64 * 64;
-  }
-  if (chunk < 64) return false;
-  p->chunk = static_cast<int>(chunk);
-  p->max_chunks = static_cast<int>((max_prefix_len + chunk - 1) / chunk);
-  // the last split of a sequence also takes the tree keys; an empty prefix
-  // still needs one partial for them
-  p->slots = p->max_chunks > 0 ? p->max_chunks : 1;
-
-  const size_t rows = static_cast<size_t>(B) * Hkv * p->slots * p->R;
-  p->o_part_off = 0;
-  p->scale_part_off = align_up(rows * D * sizeof(float), 256);
-  p->lse_part_off = align_up(p->scale_part_off + rows * sizeof(float), 256);
-  p->bytes = align_up(p->lse_part_off + rows * sizeof(float), 256);
-  return true;
+// The plan of a call on the current device.
+static bool plan_here(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p,
+                      int window = 0, int page_size = 0, long row_stride = 0) {
+  return make_plan(B, T, Hq, Hkv, D, max_prefix_len, device_cu_count(), p, window, page_size,
+                   row_stride);
 }
 
 }  // namespace ltree
 
 using ltree::Plan;
 using ltree::aligned;
+using ltree::plan_here;
 
 extern "C" {
 
@@ -119,18 +67,10 @@ int ltree_build_mask(const int32_t* parent, int B, int T, uint64_t* mask, int32_
 
 size_t ltree_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len) {
   Plan p;
-  return ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p) ? p.bytes : 0;
+  return plan_here(B, T, Hq, Hkv, D, max_prefix_len, &p) ? p.bytes : 0;
 }
 
-static int check_sizes(int B, int T, int Hq, int Hkv, int D, int max_prefix_len) {
-  if (B < 1 || T < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_prefix_len < 0) {
-    return LTREE_ERR_INVALID_ARG;
-  }
-  if (T > LTREE_MAX_TREE || (D != 64 && D != 128)) return LTREE_ERR_UNSUPPORTED;
-  // every flat index the kernels form from the query/output sizes fits in int
-  if (static_cast<long>(B) * T * Hq * D > (1L << 31) - 1) return LTREE_ERR_UNSUPPORTED;
-  return LTREE_OK;
-}
+using ltree::check_sizes;
 
 // A paged prefix: pools of pages and the table that maps each sequence's
 // keys to them (see ltree_attn_paged).
@@ -139,6 +79,12 @@ struct Paging {
   const int32_t* block_table = nullptr;
   int page_size = 0, max_pages = 0, num_pages = 0;
   uint32_t pool_bytes = 0;
+  int seq_cap = 0;
+};
+
+// Prefix row strides in elements (0, 0: packed rows of Hkv * D).
+struct Strides {
+  long k = 0, v = 0;
 };
 
 // Partials of prefix (+ tree, when has_tree) attention into the workspace;
@@ -149,7 +95,7 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
                     const int32_t* prefix_offsets, int max_prefix_len, bool has_tree,
                     const void* k_tree, const void* v_tree, const uint64_t* mask,
                     void* workspace, size_t workspace_bytes, hipStream_t stream,
-                    int window = 0, const Paging& pg = Paging()) {
+                    int window = 0, const Paging& pg = Paging(), const Strides& rs = Strides()) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
@@ -169,8 +115,11 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
       (k_prefix && !aligned(k_prefix, 16)) || (v_prefix && !aligned(v_prefix, 16))) {
     return LTREE_ERR_INVALID_ARG;
   }
+  const long packed = static_cast<long>(Hkv) * D;
+  const long kstride = rs.k > 0 ? rs.k : packed, vstride = rs.v > 0 ? rs.v : packed;
   Plan p;
-  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window, pg.page_size)) {
+  if (!plan_here(B, T, Hq, Hkv, D, max_prefix_len, &p, window, pg.page_size,
+                 kstride > vstride ? kstride : vstride)) {
     return LTREE_ERR_INVALID_ARG;
   }
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
@@ -202,6 +151,9 @@ static int partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, flo
   a.neg_inv_scale_log2 = -1.f / a.scale_log2;
   a.has_tree = has_tree ? 1 : 0;
   a.window = window;
+  a.kstride = static_cast<int>(kstride);
+  a.vstride = static_cast<int>(vstride);
+  a.seq_cap = pg.block_table != nullptr ? pg.seq_cap : p.seq_cap;
   a.seq_lens = pg.seq_lens;
   a.block_table = pg.block_table;
   a.page_size = pg.page_size;
@@ -235,7 +187,7 @@ int ltree_attn_partials(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
 static int merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
                  const int32_t* prefix_offsets, int max_prefix_len, float* o, float* lse,
                  const void* workspace, size_t workspace_bytes, hipStream_t stream,
-                 int window = 0, const Paging& pg = Paging()) {
+                 int window = 0, const Paging& pg = Paging(), const Strides& rs = Strides()) {
   if (dtype != LTREE_F32 && dtype != LTREE_BF16) return LTREE_ERR_INVALID_ARG;
   const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
   if (st != LTREE_OK) return st;
@@ -244,9 +196,11 @@ static int merge(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D,
     return LTREE_ERR_INVALID_ARG;
   }
   Plan p;
-  if (!ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, window, pg.page_size)) {
+  if (!plan_here(B, T, Hq, Hkv, D, max_prefix_len, &p, window, pg.page_size,
+                 rs.k > rs.v ? rs.k : rs.v)) {
     return LTREE_ERR_INVALID_ARG;
   }
+  if (pg.block_table != nullptr) p.seq_cap = pg.seq_cap;
   if (workspace_bytes < p.bytes || !aligned(workspace, 256)) return LTREE_ERR_WORKSPACE;
   const char* ws = static_cast<const char*>(workspace);
   const hipError_t err = ltree::launch_merge(
@@ -290,10 +244,40 @@ int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, f
                           workspace, workspace_bytes, stream);
 }
 
+size_t ltree_attn_strided_workspace_bytes(int B, int T, int Hq, int Hkv, int D,
+                                          int max_prefix_len, int64_t k_row_stride,
+                                          int64_t v_row_stride) {
+  Plan p;
+  if (ltree::check_strides(Hkv, D, k_row_stride, v_row_stride) != LTREE_OK) return 0;
+  const long s = k_row_stride > v_row_stride ? k_row_stride : v_row_stride;
+  return plan_here(B, T, Hq, Hkv, D, max_prefix_len, &p, 0, 0, s) ? p.bytes : 0;
+}
+
+int ltree_attn_strided(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                       const void* q, const void* k_prefix, const void* v_prefix,
+                       int64_t k_row_stride, int64_t v_row_stride, const int32_t* prefix_offsets,
+                       int max_prefix_len, const void* k_tree, const void* v_tree,
+                       const uint64_t* mask, float* o, float* lse, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream) {
+  if (o == nullptr || lse == nullptr) return LTREE_ERR_INVALID_ARG;
+  const int cs = ltree::check_strides(Hkv, D, k_row_stride, v_row_stride);
+  if (cs != LTREE_OK) return cs;
+  Strides rs;
+  rs.k = k_row_stride;
+  rs.v = v_row_stride;
+  const bool has_tree = k_tree != nullptr || v_tree != nullptr || mask != nullptr;
+  int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix, prefix_offsets,
+                    max_prefix_len, has_tree, k_tree, v_tree, mask, workspace, workspace_bytes,
+                    stream, 0, Paging(), rs);
+  if (st != LTREE_OK) return st;
+  return merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse, workspace,
+               workspace_bytes, stream, 0, Paging(), rs);
+}
+
 size_t ltree_window_attn_workspace_bytes(int B, int T, int Hq, int Hkv, int D, int window) {
   Plan p;
   if (window < 1) return 0;
-  return ltree::make_plan(B, T, Hq, Hkv, D, window - 1, &p, window) ? p.bytes : 0;
+  return plan_here(B, T, Hq, Hkv, D, window - 1, &p, window) ? p.bytes : 0;
 }
 
 int ltree_window_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
@@ -318,7 +302,7 @@ size_t ltree_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, int D, in
                                         int page_size) {
   Plan p;
   if (page_size < 1) return 0;
-  return ltree::make_plan(B, T, Hq, Hkv, D, max_prefix_len, &p, 0, page_size) ? p.bytes : 0;
+  return plan_here(B, T, Hq, Hkv, D, max_prefix_len, &p, 0, page_size) ? p.bytes : 0;
 }
 
 int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
@@ -331,26 +315,17 @@ int ltree_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, fl
       block_table == nullptr || seq_lens == nullptr) {
     return LTREE_ERR_INVALID_ARG;
   }
-  if (page_size < 1 || num_pages < 1 || max_pages_per_seq < 1 ||
-      max_prefix_len < 0 ||
-      static_cast<long>(max_prefix_len) > static_cast<long>(max_pages_per_seq) * page_size) {
-    return LTREE_ERR_INVALID_ARG;
-  }
-  // page rows are addressed with 64-bit offsets; a page's rows with 32-bit ones
-  if (static_cast<long>(page_size) * Hkv * D > (1L << 30)) return LTREE_ERR_UNSUPPORTED;
-  // a page size that is not a multiple of 64 addresses every row from the
-  // start of the pool with a 32-bit byte offset
-  const long pool_bytes = static_cast<long>(num_pages) * page_size * Hkv * D *
-                          (dtype == LTREE_BF16 ? 2 : 4);
-  if (page_size % 64 != 0 && pool_bytes >= (1L << 31)) return LTREE_ERR_UNSUPPORTED;
-  const bool has_tree = k_tree != nullptr || v_tree != nullptr || mask != nullptr;
   Paging pg;
+  const int cp = ltree::check_paged(dtype == LTREE_BF16 ? 2 : 4, Hkv, D, num_pages, page_size,
+                                    max_pages_per_seq, max_prefix_len, 0, &pg.pool_bytes,
+                                    &pg.seq_cap);
+  if (cp != LTREE_OK) return cp;
+  const bool has_tree = k_tree != nullptr || v_tree != nullptr || mask != nullptr;
   pg.seq_lens = seq_lens;
   pg.block_table = block_table;
   pg.page_size = page_size;
   pg.max_pages = max_pages_per_seq;
   pg.num_pages = num_pages;
-  pg.pool_bytes = static_cast<uint32_t>(pool_bytes < (1L << 31) ? pool_bytes : 0);
   int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_pages, v_pages, nullptr, max_prefix_len,
                     has_tree, k_tree, v_tree, mask, workspace, workspace_bytes, stream, 0, pg);
   if (st != LTREE_OK) return st;
@@ -362,7 +337,7 @@ size_t ltree_window_attn_paged_workspace_bytes(int B, int T, int Hq, int Hkv, in
                                                int page_size) {
   Plan p;
   if (window < 1 || page_size < 1) return 0;
-  return ltree::make_plan(B, T, Hq, Hkv, D, window - 1, &p, window, page_size) ? p.bytes : 0;
+  return plan_here(B, T, Hq, Hkv, D, window - 1, &p, window, page_size) ? p.bytes : 0;
 }
 
 int ltree_window_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
@@ -375,23 +350,20 @@ int ltree_window_attn_paged(ltree_dtype dtype, int B, int T, int Hq, int Hkv, in
       block_table == nullptr || seq_lens == nullptr) {
     return LTREE_ERR_INVALID_ARG;
   }
-  if (window < 1 || window < T || page_size < 1 || num_pages < 1 || max_pages_per_seq < 1) {
-    return LTREE_ERR_INVALID_ARG;
-  }
+  if (window < 1 || window < T) return LTREE_ERR_INVALID_ARG;
   if (window > LTREE_MAX_WINDOW) return LTREE_ERR_UNSUPPORTED;
-  if (static_cast<long>(page_size) * Hkv * D > (1L << 30)) return LTREE_ERR_UNSUPPORTED;
   // a window starts at any key, so rows are addressed lane by lane from the
-  // start of the pool (32-bit byte offsets)
-  const long pool_bytes = static_cast<long>(num_pages) * page_size * Hkv * D *
-                          (dtype == LTREE_BF16 ? 2 : 4);
-  if (pool_bytes >= (1L << 31)) return LTREE_ERR_UNSUPPORTED;
+  // start of the pool (32-bit byte offsets); a sequence longer than the block
+  // table reaches gives NaN rows, like an over-long sequence of ltree_attn_paged
   Paging pg;
+  const int cp = ltree::check_paged(dtype == LTREE_BF16 ? 2 : 4, Hkv, D, num_pages, page_size,
+                                    max_pages_per_seq, 0, window, &pg.pool_bytes, &pg.seq_cap);
+  if (cp != LTREE_OK) return cp;
   pg.seq_lens = seq_lens;
   pg.block_table = block_table;
   pg.page_size = page_size;
   pg.max_pages = max_pages_per_seq;
   pg.num_pages = num_pages;
-  pg.pool_bytes = static_cast<uint32_t>(pool_bytes);
   int st = partials(dtype, B, T, Hq, Hkv, D, scale, q, k_pages, v_pages, nullptr, window - 1,
                     true, k_tree, v_tree, mask, workspace, workspace_bytes, stream, window, pg);
   if (st != LTREE_OK) return st;

@@ -6,42 +6,18 @@
 #include <stdint.h>
 
 #include "ltree.h"
+#include "ltree_plan.h"
 
 namespace ltree {
 
-// How one ltree_attn call is cut into work.  Derived only from the sizes and
-// the device's compute-unit count, so the workspace size query and the calls
-// that use the workspace always agree.
-struct Plan {
-  int B, T, Hq, Hkv, D, G, R;  // R = G*T query rows per (sequence, KV head)
-  int max_prefix_len;
-  int window;      // 0, or the sliding window W (then max_prefix_len = W - 1)
-  int chunk;       // prefix keys per split (multiple of 64)
-  int max_chunks;  // ceil(max_prefix_len / chunk): prefix splits per (b, g)
-  int slots;       // max(max_chunks, 1).  Slot s of sequence b holds prefix
-                   // keys [s*chunk, min((s+1)*chunk, L_b)); its last
-                   // non-empty slot (slot 0 when L_b = 0) also the T tree keys
-  size_t o_part_off, scale_part_off, lse_part_off, bytes;  // workspace layout
-};
-
-// Page numbers of one split that the paged kernels hold in LDS: a split
-// covers at most (kMaxSplitPages - 1) * page_size keys.
-constexpr int kMaxSplitPages = 448;
-
-// Returns false when the sizes are invalid (the caller reports the status).
-// With window > 0 the prefix part of each sequence is at most its last
-// window - 1 keys, and max_prefix_len is taken as window - 1.
-// page_size > 0: a paged prefix (any page size); splits are capped so their
-// pages fit the kernels' LDS table.
-bool make_plan(int B, int T, int Hq, int Hkv, int D, int max_prefix_len, Plan* p, int window = 0,
-               int page_size = 0);
-
 // The prefix keys sequence b's partials read, [start, start + n) of its L_b
-// packed rows.  Without a window all of them (false when L_b is out of range:
-// negative or above max_prefix_len); with a window W the last min(L_b, W - 1),
-// the cache keys a token at the tree's first position can see.
-__device__ inline bool key_range(int L, int window, int max_prefix_len, int* start, int* n) {
-  if (L < 0 || (window == 0 && L > max_prefix_len)) return false;
+// rows.  Without a window all of them; with a window W the last
+// min(L_b, W - 1), the cache keys a token at the tree's first position can
+// see.  False when L_b is out of range: negative, above seq_cap (what a paged
+// call's block table can address), or (no window) above max_prefix_len.
+__device__ inline bool key_range(int L, int window, int max_prefix_len, int seq_cap, int* start,
+                                 int* n) {
+  if (L < 0 || L > seq_cap || (window == 0 && L > max_prefix_len)) return false;
   *n = window > 0 ? min(L, window - 1) : L;
   *start = L - *n;
   return true;
@@ -74,9 +50,13 @@ struct PartialArgs {
   int B, T, Hq, Hkv, G, R;
   int W;             // mask words per row, ceil(T / 64)
   int chunk, max_chunks, slots, max_prefix_len;
+  int seq_cap;       // largest L_b the call may address
   int rows_per_wg, row_blocks;
   int has_tree;      // 0: prefix keys only (no tree part; the tree arguments are unused)
   int window;        // 0, or W: node i sees the last W - depth(i) prefix keys (and its branch)
+  // prefix row strides in elements (key j, KV head g at row (off + j) * stride
+  // + g * D); the packed layout has Hkv * D.  Tree rows are always packed.
+  int kstride, vstride;
   // paged prefix (block_table != nullptr): kp/vp are page pools
   // [num_pages][page_size][Hkv][D]; key j of sequence b is row j % page_size
   // of page block_table[b * max_pages + j / page_size]; L_b = seq_lens[b]
