@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define LTREE_VERSION 120 /* 1.2.0: strided prefix caches */
+#define LTREE_VERSION 130 /* 1.3.0: ltree_attn_noalloc */
 #define LTREE_MAX_TREE 256 /* largest tree; a mask row has W = ceil(T / 64) 64-bit words */
 #define LTREE_MAX_WINDOW (1 << 20) /* largest sliding window of ltree_window_attn */
 
@@ -53,7 +53,9 @@ typedef enum {
   LTREE_ERR_INVALID_ARG = -1, /* null pointer, bad size, Hq % Hkv != 0, scale <= 0, ... */
   LTREE_ERR_UNSUPPORTED = -2, /* valid but not built: D not 64/128, T > 256, ...       */
   LTREE_ERR_WORKSPACE = -3,   /* workspace too small or misaligned                     */
-  LTREE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed            */
+  LTREE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed            */
+  LTREE_ERR_SCRATCH = -5      /* ltree_attn_noalloc: the call needs more scratch memory
+                                 than LTREE_NOALLOC_SCRATCH_BYTES                       */
 } ltree_status;
 
 typedef enum {
@@ -157,6 +159,37 @@ int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float sc
                const void* k_tree, const void* v_tree, const uint64_t* mask,
                float* o, float* lse, void* workspace, size_t workspace_bytes,
                hipStream_t stream);
+
+/*
+ * ltree_attn_noalloc -- ltree_attn for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The same kernels and the same results as ltree_attn
+ * with the same arguments; the partials live in a static device array of
+ * LTREE_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs
+ * on, from the first call on that device until the process ends, instead of
+ * a workspace argument.  The call allocates nothing.
+ *
+ *   arguments      as for ltree_attn, without the workspace.
+ *   stream         must belong to the current device (the one whose copy of
+ *                  the array is used); LTREE_ERR_INVALID_ARG otherwise.
+ *
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (on different streams, or from different threads with
+ * their kernels still running) race and give wrong results.  Calls ordered on
+ * one stream are safe.  Nothing in the array has to start at zero: the
+ * partial kernel writes every value the merge reads.
+ *
+ * Returns as ltree_attn, and LTREE_ERR_SCRATCH when
+ * ltree_attn_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len) exceeds
+ * LTREE_NOALLOC_SCRATCH_BYTES (nothing is launched then).  Two kernel
+ * launches on `stream`.
+ */
+#define LTREE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20) /* 96 MiB per device */
+int ltree_attn_noalloc(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                       const void* q, const void* k_prefix, const void* v_prefix,
+                       const int32_t* prefix_offsets, int max_prefix_len,
+                       const void* k_tree, const void* v_tree, const uint64_t* mask,
+                       float* o, float* lse, hipStream_t stream);
 
 /*
  * ltree_attn_strided_workspace_bytes -- workspace size of ltree_attn_strided

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
               "ltree_window_attn_workspace_bytes", "ltree_attn_paged",
               "ltree_attn_paged_workspace_bytes", "ltree_window_attn_paged",
               "ltree_window_attn_paged_workspace_bytes", "ltree_tree_rope", "ltree_commit_kv",
-              "ltree_attn_strided", "ltree_attn_strided_workspace_bytes"):
+              "ltree_attn_strided", "ltree_attn_strided_workspace_bytes",
+              "ltree_attn_noalloc"):
         assert n in names
 
 
@@ -47,9 +48,10 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     import tree_attention_amd as ta
-    assert ta.ltree_version() == 120
+    assert ta.ltree_version() == 130
     assert ta.ltree_status_string(0) == "ok"
     assert "workspace" in ta.ltree_status_string(ta.LTREE_ERR_WORKSPACE)
+    assert "scratch" in ta.ltree_status_string(ta.LTREE_ERR_SCRATCH)
     assert ta.ltree_status_string(12345) == "unknown status"
 
 
@@ -129,3 +131,36 @@ def test_strided_argument_errors(ks, vs, expect):
     st = fn(1, 1, 8, 8, 8, 128, 0.1, 0x1000, 0x2000, 0x3000, ks, vs, 0x4000, 100, 0x5000,
             0x6000, 0x7000, 0x8000, 0x9000, 0x100000, 16, None)
     assert st == expect
+
+
+def test_noalloc_scratch_limit_matches_header():
+    import tree_attention_amd as ta
+    src = open(HEADER).read()
+    m = re.search(r"#define LTREE_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == ta.LTREE_NOALLOC_SCRATCH_BYTES
+    # the five benchmark workloads fit; a 256-node tree over 32768 keys does not
+    for sizes in [(1, 8, 4, 4, 64, 512), (1, 64, 32, 8, 128, 16384), (1, 64, 32, 8, 128, 131072),
+                  (1, 64, 40, 8, 128, 32768), (4, 32, 32, 8, 128, 131072)]:
+        assert 0 < ta.ltree_attn_workspace_bytes(*sizes) <= ta.LTREE_NOALLOC_SCRATCH_BYTES
+    assert ta.ltree_attn_workspace_bytes(1, 256, 40, 8, 128, 32768) > ta.LTREE_NOALLOC_SCRATCH_BYTES
+
+
+@no_gpu
+def test_noalloc_argument_errors():
+    """Rejected before any HIP call: bad sizes, and partials beyond the array."""
+    lib, ta = _raw()
+    fn = lib.ltree_attn_noalloc
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fn.restype = I
+    fn.argtypes = [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, P, P]
+    fake = P(1 << 20)
+
+    def call(B=1, T=64, Hq=40, Hkv=8, D=128, L=32768):
+        return fn(ta.LTREE_BF16, B, T, Hq, Hkv, D, 0.088, fake, fake, fake, fake, L, fake, fake,
+                  fake, fake, fake, None)
+
+    assert call(B=0) == ta.LTREE_ERR_INVALID_ARG
+    assert call(Hkv=7) == ta.LTREE_ERR_INVALID_ARG
+    assert call(D=96) == ta.LTREE_ERR_UNSUPPORTED
+    assert call(T=256) == ta.LTREE_ERR_SCRATCH
+    assert call(B=8) == ta.LTREE_ERR_SCRATCH

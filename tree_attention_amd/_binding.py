@@ -24,12 +24,14 @@ LTREE_ERR_INVALID_ARG = -1
 LTREE_ERR_UNSUPPORTED = -2
 LTREE_ERR_WORKSPACE = -3
 LTREE_ERR_HIP = -4
+LTREE_ERR_SCRATCH = -5
+LTREE_NOALLOC_SCRATCH_BYTES = 96 << 20
 LTREE_F32 = 0
 LTREE_BF16 = 1
 LTREE_MAX_TREE = 256
 
 EXPORTED = ("ltree_version", "ltree_status_string", "ltree_build_mask",
-            "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_partials",
+            "ltree_attn_workspace_bytes", "ltree_attn", "ltree_attn_noalloc", "ltree_attn_partials",
             "ltree_attn_merge", "ltree_prefix_attn", "ltree_attn_strided_workspace_bytes",
             "ltree_attn_strided", "ltree_attn_paged_workspace_bytes",
             "ltree_attn_paged", "ltree_window_attn_paged_workspace_bytes",
@@ -57,6 +59,7 @@ def _load() -> ctypes.CDLL:
         "ltree_build_mask": (I, [P, I, I, P, P, P]),
         "ltree_attn_workspace_bytes": (S, [I, I, I, I, I, I]),
         "ltree_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, P, P, S, P]),
+        "ltree_attn_noalloc": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, P, P]),
         "ltree_attn_partials": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, P, S, P]),
         "ltree_attn_merge": (I, [I, I, I, I, I, I, P, I, P, P, P, S, P]),
         "ltree_prefix_attn": (I, [I, I, I, I, I, I, F, P, P, P, P, I, P, P, P, S, P]),
@@ -217,6 +220,24 @@ def ltree_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_
         _ptr(prefix_offsets), int(max_prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask),
         _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream))
+
+
+def ltree_attn_noalloc(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, k_tree, v_tree,
+                       mask, o, lse, scale, stream=None) -> int:
+    """ltree_attn with its partials in the library's static per-device array
+    (no workspace argument; nothing is allocated)."""
+    B, T, Hq, Hkv, D = _check_attn_inputs(q, k_prefix, v_prefix, prefix_offsets, k_tree,
+                                          v_tree, mask)
+    _dev(o, "o", torch.float32)
+    _dev(lse, "lse", torch.float32)
+    if o.shape != (B, T, Hq, D) or lse.shape != (B, Hq, T):
+        raise ValueError("o must be [B, T, Hq, D] and lse [B, Hq, T]")
+    kp = k_prefix if k_prefix.numel() else None
+    vp = v_prefix if v_prefix.numel() else None
+    return _lib.ltree_attn_noalloc(
+        _dtype_code(q), B, T, Hq, Hkv, D, float(scale), _ptr(q), _ptr(kp), _ptr(vp),
+        _ptr(prefix_offsets), int(max_prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask),
+        _ptr(o), _ptr(lse), _stream(stream))
 
 
 def ltree_prefix_attn(q, k_prefix, v_prefix, prefix_offsets, max_prefix_len, o, lse, workspace,

@@ -5,11 +5,18 @@
 
 #include "ltree_internal.h"
 
+// The partials of ltree_attn_noalloc: each device the library runs on holds
+// its own copy from the first call there until the process ends.  In host
+// code this name is a stand-in, not a device address: kernels get the
+// address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) char scratch[LTREE_NOALLOC_SCRATCH_BYTES];
+
 namespace ltree {
 
 namespace {
 constexpr int kMaxDevices = 64;
-std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+std::atomic<int> g_cu_count[kMaxDevices];        // 0 = not queried yet
+std::atomic<void*> g_scratch_ptr[kMaxDevices];   // nullptr = not looked up yet
 }  // namespace
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -17,14 +24,26 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 int device_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev >= kMaxDevices) dev = kMaxDevices - 1;
-  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  const bool cached = dev < kMaxDevices;  // devices past the table are asked every time
+  int n = cached ? g_cu_count[dev].load(std::memory_order_relaxed) : 0;
   if (n > 0) return n;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
     n = 256;
   }
-  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  if (cached) g_cu_count[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+// Device address of device dev's copy of `scratch` (dev current), looked up
+// once per device; nullptr if the lookup fails.
+static void* scratch_on(int dev) {
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  return ptr;
 }
 
 // The plan of a call on the current device.
@@ -51,6 +70,7 @@ const char* ltree_status_string(int status) {
     case LTREE_ERR_UNSUPPORTED: return "unsupported size or dtype";
     case LTREE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case LTREE_ERR_HIP: return "HIP runtime error";
+    case LTREE_ERR_SCRATCH: return "needs more scratch than LTREE_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }
@@ -229,6 +249,31 @@ int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float sc
   if (st != LTREE_OK) return st;
   return ltree_attn_merge(dtype, B, T, Hq, Hkv, D, prefix_offsets, max_prefix_len, o, lse,
                           workspace, workspace_bytes, stream);
+}
+
+int ltree_attn_noalloc(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
+                       const void* q, const void* k_prefix, const void* v_prefix,
+                       const int32_t* prefix_offsets, int max_prefix_len, const void* k_tree,
+                       const void* v_tree, const uint64_t* mask, float* o, float* lse,
+                       hipStream_t stream) {
+  const int st = check_sizes(B, T, Hq, Hkv, D, max_prefix_len);
+  if (st != LTREE_OK) return st;
+  Plan p;
+  if (!plan_here(B, T, Hq, Hkv, D, max_prefix_len, &p)) return LTREE_ERR_INVALID_ARG;
+  if (p.bytes > LTREE_NOALLOC_SCRATCH_BYTES) return LTREE_ERR_SCRATCH;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LTREE_ERR_HIP;
+  if (dev >= ltree::kMaxDevices) return LTREE_ERR_UNSUPPORTED;
+  if (stream != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return LTREE_ERR_HIP;
+    if (sdev != dev) return LTREE_ERR_INVALID_ARG;
+  }
+  void* ws = ltree::scratch_on(dev);
+  if (ws == nullptr) return LTREE_ERR_HIP;
+  return ltree_attn(dtype, B, T, Hq, Hkv, D, scale, q, k_prefix, v_prefix, prefix_offsets,
+                    max_prefix_len, k_tree, v_tree, mask, o, lse, ws, LTREE_NOALLOC_SCRATCH_BYTES,
+                    stream);
 }
 
 int ltree_prefix_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float scale,
