@@ -53,8 +53,15 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 REPS = 7                    # extra replays of the timed graphs for median / minimum
 METRIC = "tree-verify attn µs/call + TFLOP/s @L=32k,T=64; % MFMA / HBM roofline"
 KERNEL_SOURCES = ["attn_partial_mfma_impl.h", "attn_partial_mfma.hip", "ltree_api.hip",
-                  "ltree_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_partials_qwq32b_L32k_T64.json")
+                  "ltree_internal.h", "ltree_plan.cpp", "ltree_plan.h"]
+# HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the partial kernel),
+# one per benchmark workload; written by --traffic-summary
+TRAFFIC_SLUG = {2: "llama3_8b_L16k_T64", 3: "llama3_8b_L128k_T64", 4: "qwq32b_L32k_T64",
+                5: "ragged_b4_L8k_128k_T32"}
+
+
+def traffic_file(config: int) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_partials_{TRAFFIC_SLUG.get(config, config)}.json")
 
 
 def log(*a):
@@ -135,10 +142,23 @@ def cpu_baseline(w, budget_s=15.0, min_s=10.0):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"fp64 NumPy oracle, {what} ({passes:.2f} x {Hkv} KV heads, {Hq} query heads, "
                   f"all {T} tree rows, full {sum(w.prefix_lens)}-key prefix), {t_total:.2f} s "
-                  f"wall; matmuls on {threads} BLAS threads, exp single-threaded",
+                  f"wall; NumPy on {threads} BLAS threads",
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_graph(fn, K):
@@ -516,6 +536,170 @@ ROWS = {"xattn": row_xattn, "window": row_window, "bigtree": row_bigtree, "paged
         "commit": row_commit, "rope": row_rope}
 
 
+def _kernel_kind(name: str):
+    if "partial_mfma_kernel" in name or "partial_simple_kernel" in name:
+        return "partial"
+    if "lse_merge_kernel" in name:
+        return "merge"
+    return None
+
+
+def _short_name(name: str) -> str:
+    """A kernel's name without namespace, return type and parameter list."""
+    name = name.replace("void ", "").replace("ltree::(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def _stats(xs):
+    if not xs:
+        return "-"
+    return f"{statistics.mean(xs):.2f} / {min(xs):.2f} / {max(xs):.2f}"
+
+
+def trace_summary(path: str, K: int, W: int) -> str:
+    """Per-phase durations of the attention kernels in a rocprofv3 kernel trace
+    (`--kernel-trace --output-format csv`, the *_kernel_trace.csv file) of
+    `bench.py --config k --steps K --warmup W` (neither --hot nor --row).
+    main() launches, in this order: W warm-up steps, the step graph (one
+    untimed and one timed replay), K eager steps, REPS more replays of the
+    step graph, the hot graph over one KV copy (one untimed and REPS timed
+    replays) and the graph of the partial kernel alone (one untimed and REPS
+    timed replays).  Returns a markdown table."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            kind = _kernel_kind(r["Kernel_Name"])
+            if kind:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), kind))
+    rows.sort()
+    per_step = 2 if any(k == "merge" for _, _, k in rows) else 1
+    phases = [("warm-up steps, eager", W, "cold"), ("step graph, untimed replay", K, "cold"),
+              ("step graph, timed replay (`us_per_call`)", K, "cold"),
+              ("eager steps (`us_per_call_eager`)", K, "cold"),
+              (f"step graph, {REPS} more replays (`cold_median`)", REPS * K, "cold"),
+              ("hot graph, untimed replay", K, "hot"),
+              (f"hot graph, {REPS} replays (`hot_median`)", REPS * K, "hot"),
+              ("partial kernel graph, untimed replay", K, "cold"),
+              (f"partial kernel graph, {REPS} replays (`roofline.kernel_us`)", REPS * K, "cold")]
+    lines = ["| phase | cache | steps | partial kernel avg / min / max (us) | merge avg / min / max (us) "
+             "| first start to last end, per step (us) |", "|---|---|---:|---:|---:|---:|"]
+    pos = 0
+    cold = {"partial": [], "merge": []}
+    for name, steps, cache in phases:
+        n = steps * (1 if name.startswith("partial kernel") else per_step)
+        seg = rows[pos:pos + n]
+        pos += n
+        if len(seg) < n:
+            raise SystemExit(f"trace has {len(rows)} attention launches, fewer than the phases need")
+        p = [(e - s) / 1000 for s, e, k in seg if k == "partial"]
+        m = [(e - s) / 1000 for s, e, k in seg if k == "merge"]
+        if cache == "cold" and name != "warm-up steps, eager":
+            cold["partial"] += p
+            cold["merge"] += m
+        span = (seg[-1][1] - seg[0][0]) / 1000 / steps
+        lines.append(f"| {name} | {cache} | {steps} | {_stats(p)} | {_stats(m)} | {span:.2f} |")
+    if pos != len(rows):
+        raise SystemExit(f"trace has {len(rows)} attention launches, the phases account for {pos}")
+    lines.append(f"| all cold launches after the warm-up | cold | | {_stats(cold['partial'])} "
+                 f"| {_stats(cold['merge'])} | |")
+    return "\n".join(lines)
+
+
+def _counter_means(path: str, counter: str):
+    """Per-kernel mean over dispatches of one counter in a rocprofv3
+    *_counter_collection.csv (values of one dispatch summed first)."""
+    import csv
+    per = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {name: (sum(v) / len(v), len(v)) for name, v in out.items()}
+
+
+def traffic_summary(config: int, fetch_csv: str, write_csv: str, copy_fetch_csv: str,
+                    copy_write_csv: str, copy_mib: int = 256) -> str:
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs (KiB
+    per dispatch) of `bench.py --config k`, each scaled by what the same counter
+    reads for the runtime's copy kernel moving `copy_mib` MiB (`bench.py
+    --copy-probe`).  Writes the partial kernel's record (read by the bench
+    while the kernel sources hash the same) and returns a markdown table."""
+    from workloads import CONFIGS, make_config
+    copy_bytes = copy_mib << 20
+    cf = _counter_means(copy_fetch_csv, "FETCH_SIZE")
+    cw = _counter_means(copy_write_csv, "WRITE_SIZE")
+    ck = next(n for n in cf if "copyBuffer" in n)
+    fetch_scale = copy_bytes / (cf[ck][0] * 1024)
+    write_scale = copy_bytes / (cw[ck][0] * 1024)
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+    w = make_config(config)
+    _, bytes_alg, bytes_partials = algorithmic_counts(w)
+    lines = [f"Calibration: `__amd_rocclr_copyBuffer` moving {copy_mib} MiB reads FETCH_SIZE = "
+             f"{cf[ck][0]:.1f} KiB and WRITE_SIZE = {cw[ck][0]:.1f} KiB per launch: scale "
+             f"{fetch_scale:.4f} and {write_scale:.4f}.", "",
+             "| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | read MB | written MB |",
+             "|---|---:|---:|---:|---:|---:|"]
+    rec = None
+    for name in sorted(fetch, key=lambda n: -fetch[n][0]):
+        kind = _kernel_kind(name)
+        if kind is None:
+            continue
+        fk, n = fetch[name]
+        wk = write.get(name, (0.0, 0))[0]
+        rb, wb = fk * 1024 * fetch_scale, wk * 1024 * write_scale
+        short = _short_name(name)
+        lines.append(f"| `{short}` | {n} | {fk:.1f} | {wk:.1f} | {rb / 1e6:.2f} | {wb / 1e6:.2f} |")
+        if kind == "partial" and rec is None:
+            rec = {"kernel": short, "config": config, "workload": CONFIGS[config]["name"],
+                   "kernel_hash": kernel_hash(), "fetch_kib_raw": round(fk, 3),
+                   "write_kib_raw": round(wk, 3), "fetch_scale": round(fetch_scale, 4),
+                   "write_scale": round(write_scale, 4), "bytes_per_launch": int(rb + wb),
+                   "fetch_bytes": int(rb), "write_bytes": int(wb),
+                   "algorithmic_bytes": int(bytes_partials)}
+    lines += ["", f"Algorithmic bytes: partial kernel {bytes_partials / 1e6:.2f} MB (prefix K/V, queries, "
+              f"tree K/V, mask); whole call {bytes_alg / 1e6:.2f} MB (adds the outputs)."]
+    if rec is not None:
+        with open(traffic_file(config), "w") as f:
+            json.dump(rec, f, indent=1)
+        lines.append(f"Partial kernel: {rec['bytes_per_launch'] / 1e6:.2f} MB per launch = "
+                     f"{rec['bytes_per_launch'] / bytes_partials:.3f} x its algorithmic bytes.")
+    return "\n".join(lines)
+
+
+def counter_summary(paths) -> str:
+    """Per-dispatch means of every counter in rocprofv3 *_counter_collection.csv
+    files, for the attention kernels.  Returns a markdown table."""
+    import csv
+    names, table = [], {}
+    for path in paths:
+        with open(path) as f:
+            counters = sorted({r["Counter_Name"] for r in csv.DictReader(f)})
+        for c in counters:
+            for kname, (mean, n) in _counter_means(path, c).items():
+                if _kernel_kind(kname) is None:
+                    continue
+                short = _short_name(kname)
+                table.setdefault(short, {})[c] = (mean, n)
+                if c not in names:
+                    names.append(c)
+    lines = ["| counter | " + " | ".join(f"`{k}`" for k in table) + " |",
+             "|---|" + "---:|" * len(table)]
+    for c in names:
+        cells = []
+        for k in table:
+            v = table[k].get(c)
+            cells.append(f"{v[0]:.4g} ({v[1]})" if v else "-")
+        lines.append(f"| {c} | " + " | ".join(cells) + " |")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,7 +712,27 @@ def main():
                     help="only copy a MIB-MiB buffer 5 times (calibrates HBM byte counters)")
     ap.add_argument("--row", choices=sorted(ROWS), default=None,
                     help="measure one of the steps around the verification path instead")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV", default=None,
+                    help="print per-phase kernel durations of a rocprofv3 trace of this bench "
+                         "run (same --steps/--warmup) and exit; no GPU needed")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE/WRITE_SIZE runs of this bench run and "
+                         "of --copy-probe 256 (counter_collection.csv files), write the traffic "
+                         "record of --config and exit; no GPU needed")
+    ap.add_argument("--counter-summary", nargs="+", metavar="COUNTER_CSV", default=None,
+                    help="print per-dispatch means of the counters in rocprofv3 "
+                         "counter_collection.csv files and exit; no GPU needed")
     args = ap.parse_args()
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
+        return
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.steps, args.warmup))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(args.config, *args.traffic_summary))
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -687,8 +891,9 @@ def main():
     tflops = flop / (us * 1e-6) / 1e12
     part_tflops = flop / (part_us * 1e-6) / 1e12
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE))
+    tfile = traffic_file(args.config)
+    if os.path.exists(tfile):
+        rec = json.load(open(tfile))
         if rec.get("kernel_hash") == kernel_hash() and rec.get("config") == args.config:
             traffic = rec.get("bytes_per_launch")
 
