@@ -52,10 +52,12 @@
 // three V^T buffers [D][64 keys] (exact for |v| < 65504).  Probabilities
 // enter the P.V product as fp16, whose rounding (2^-11) keeps the output
 // within tolerance even where a few large values dominate a row, which bf16
-// (2^-8) does not.  LDS has 64 banks of 4 bytes (16 lanes per cycle for
-// 16-byte accesses, 64 for 4-byte ones); the K chunk swizzle and the V^T row
-// pitch and cell swizzle make every operand read and every V^T write
-// conflict-free.  One barrier per tile.
+// (2^-8) does not.  LDS has 64 banks of 4 bytes.  The K chunk swizzle puts
+// the 16 lanes of a lane group on 16 different 16-byte bank groups, so the K
+// operand reads have no bank conflicts; the V^T buffers use a 144-byte row
+// pitch and a cell swizzle, and their reads and the transposed writes still
+// register a few conflict cycles per instruction (measured), most of which the
+// LDS pipeline hides.  One barrier per tile.
 //
 // Shared by the translation units that instantiate the kernel's variants
 // (attn_partial_mfma*.hip), so that they compile in parallel.
