@@ -940,6 +940,9 @@ def main():
             "kernel_us": round(part_us, 2),
             "kernel_us_min": round(min(part_all), 2),
             "hbm_frac": round(bytes_partials / (part_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            # the whole call (partial kernel and merge) against the same peaks
+            "call_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "call_hbm_frac": round(bytes_alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },
     }
     if not args.no_cpu_baseline:
