@@ -92,7 +92,9 @@ const char* ltree_status_string(int status);
  *           rows of a tree with an invalid entry are written as zero.
  *
  * Returns LTREE_OK, LTREE_ERR_INVALID_ARG (null pointer, B < 1, T < 1),
- * LTREE_ERR_UNSUPPORTED (T > 256) or LTREE_ERR_HIP.  One launch, no workspace.
+ * LTREE_ERR_UNSUPPORTED (T > 256) or LTREE_ERR_HIP.  No workspace; one launch,
+ * or (more than 16 trees, or T > 64) one launch spread over workgroups and,
+ * when status is requested, a one-wave launch that forms it.
  */
 int ltree_build_mask(const int32_t* parent, int B, int T, uint64_t* mask,
                      int32_t* status, hipStream_t stream);

@@ -154,3 +154,17 @@ def test_window_wide_tree(name, B, T, lens, trees, dtype, window):
     tol = 2e-2 if dtype == "bf16" else 1e-4
     assert np.max(np.abs(o.cpu().double().numpy() - o_ref)) <= tol
     assert np.max(np.abs(lse.cpu().double().numpy() - lse_ref)) <= LSE_TOL
+
+
+def test_mask_wide_many_trees_invalid():
+    """40 wide trees, one workgroup each; status from the spread build."""
+    rng = np.random.default_rng(8)
+    parent = np.stack([make_tree(rng, 200, ("bounded", 12, 3)) for _ in range(40)])
+    parent[33, 150] = 180
+    parent[21, 199] = -5
+    say("mask wide 40 trees, invalid entries")
+    got, st = _mask(parent)
+    assert st == 1 + 21 * 200 + 199
+    ok = [b for b in range(40) if b not in (21, 33)]
+    assert np.array_equal(got[ok], oracle.oracle_mask(parent[ok]))
+    assert not got[[21, 33]].any()

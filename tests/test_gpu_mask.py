@@ -62,3 +62,31 @@ def test_mask_many_trees():
     got, st = _build(parent)
     assert st == 0
     assert np.array_equal(got, oracle.oracle_mask(parent)[:, :, 0])
+
+
+def test_mask_many_trees_invalid_status():
+    """300 trees spread over workgroups: the status names the first invalid
+    entry of the first invalid tree, every other tree is built."""
+    rng = np.random.default_rng(6)
+    parent = np.stack([make_tree(rng, 64, ("bounded", 8, 3)) for _ in range(300)])
+    parent[250, 3] = 7      # a later node
+    parent[137, 40] = 40    # self-parent
+    parent[137, 12] = -2    # below -1: the first invalid entry of tree 137
+    say("mask 300 trees, invalid entries")
+    got, st = _build(parent)
+    assert st == 1 + 137 * 64 + 12
+    ok = [b for b in range(300) if b not in (137, 250)]
+    assert np.array_equal(got[ok], oracle.oracle_mask(parent[ok])[:, :, 0])
+    assert not got[[137, 250]].any()
+
+
+def test_mask_seventeen_trees_first_tree_invalid():
+    """The smallest batch that takes the spread build, with tree 0 invalid."""
+    rng = np.random.default_rng(7)
+    parent = np.stack([make_tree(rng, 33, "uniform") for _ in range(17)])
+    parent[0, 32] = 32
+    say("mask 17 trees, tree 0 invalid")
+    got, st = _build(parent)
+    assert st == 1 + 32
+    assert np.array_equal(got[1:], oracle.oracle_mask(parent[1:])[:, :, 0])
+    assert not got[0].any()

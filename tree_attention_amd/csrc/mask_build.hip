@@ -16,6 +16,15 @@
 // Trees of 65..256 nodes (W = ceil(T/64) words per row) take the same pointer
 // jumping with one thread per node of a 256-thread workgroup, A_i held as W
 // words, the previous round's values exchanged through LDS, and eight rounds.
+//
+// Up to 16 trees of at most 64 nodes take one workgroup, which also forms the
+// status word (the smallest invalid entry over all trees).  More trees, or
+// trees of more than 64 nodes, are spread over workgroups (16 trees, or one
+// wide tree, each), and a one-wave kernel forms the status afterwards: the
+// rows of a tree with an invalid entry are all zero, while row 0 of a valid
+// tree always holds bit 0, so the first tree whose row 0 is zero is the first
+// invalid one, and its parent entries give the first invalid index.
+#include <algorithm>
 #include <climits>
 
 #include "ltree_internal.h"
@@ -29,6 +38,7 @@ __device__ inline uint64_t shfl_u64(uint64_t v, int src) {
   return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
+// status != nullptr only for a one-workgroup launch
 __global__ __launch_bounds__(1024) void mask_build_kernel(const int32_t* __restrict__ parent,
                                                           int B, int T,
                                                           uint64_t* __restrict__ mask,
@@ -42,7 +52,7 @@ __global__ __launch_bounds__(1024) void mask_build_kernel(const int32_t* __restr
   const int nwaves = blockDim.x >> 6;
   const bool node = lane < T;
 
-  for (int b = wave; b < B; b += nwaves) {
+  for (int b = blockIdx.x * nwaves + wave; b < B; b += gridDim.x * nwaves) {
     const size_t row0 = static_cast<size_t>(b) * T;
     int p = -1;
     bool bad = false;
@@ -80,6 +90,7 @@ __global__ __launch_bounds__(1024) void mask_build_kernel(const int32_t* __restr
 constexpr int kWideThreads = 256;  // nodes of the largest tree
 constexpr int kWideWords = 4;      // mask words per row of the largest tree
 
+// status != nullptr only for a one-workgroup launch
 __global__ __launch_bounds__(kWideThreads) void mask_build_wide_kernel(
     const int32_t* __restrict__ parent, int B, int T, int W, uint64_t* __restrict__ mask,
     int32_t* __restrict__ status) {
@@ -91,7 +102,7 @@ __global__ __launch_bounds__(kWideThreads) void mask_build_wide_kernel(
   __syncthreads();
   const bool node = i < T;
 
-  for (int b = 0; b < B; ++b) {
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
     const size_t row0 = static_cast<size_t>(b) * T;
     int p = -1;
     bool bad = false;
@@ -128,21 +139,65 @@ __global__ __launch_bounds__(kWideThreads) void mask_build_wide_kernel(
   }
 }
 
+// The status word after a build spread over workgroups (one wave): the
+// first tree whose row 0 is zero, then its first invalid parent entry.
+__global__ __launch_bounds__(64) void mask_status_kernel(const int32_t* __restrict__ parent, int B,
+                                                         int T, int W,
+                                                         const uint64_t* __restrict__ mask,
+                                                         int32_t* __restrict__ status) {
+  const int lane = threadIdx.x;
+  int first = INT_MAX;
+  for (int b = lane; b < B; b += 64) {
+    if (mask[static_cast<size_t>(b) * T * W] == 0ull) {
+      first = b;
+      break;
+    }
+  }
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) first = min(first, __shfl_xor(first, s));
+  int st = 0;
+  if (first != INT_MAX) {
+    const size_t row0 = static_cast<size_t>(first) * T;
+    int bad_i = INT_MAX;
+    for (int i = lane; i < T; i += 64) {
+      const int p = parent[row0 + i];
+      if (p < -1 || p >= i) {
+        bad_i = i;
+        break;
+      }
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) bad_i = min(bad_i, __shfl_xor(bad_i, s));
+    st = static_cast<int>(row0) + bad_i + 1;
+  }
+  if (lane == 0) *status = st;
+}
+
 }  // namespace
 
 hipError_t launch_mask_build(const int32_t* parent, int B, int T, uint64_t* mask,
                              int32_t* status, hipStream_t stream) {
-  // One workgroup: the status word needs the minimum over all trees, and the
-  // mask is built once per verification step, so B trees per 16 waves is ample.
-  if (T > 64) {
-    hipLaunchKernelGGL(mask_build_wide_kernel, dim3(1), dim3(kWideThreads), 0, stream, parent, B,
-                       T, (T + 63) / 64, mask, status);
+  const int W = (T + 63) / 64;
+  if (T <= 64 && B <= 16) {  // one workgroup, status formed in place
+    hipLaunchKernelGGL(mask_build_kernel, dim3(1), dim3(64 * B), 0, stream, parent, B, T, mask,
+                       status);
     return hipGetLastError();
   }
-  const int waves = B < 16 ? B : 16;
-  hipLaunchKernelGGL(mask_build_kernel, dim3(1), dim3(64 * waves), 0, stream, parent, B, T,
-                     mask, status);
-  return hipGetLastError();
+  if (T <= 64) {
+    const int wgs = std::min((B + 15) / 16, 1024);
+    hipLaunchKernelGGL(mask_build_kernel, dim3(wgs), dim3(1024), 0, stream, parent, B, T, mask,
+                       static_cast<int32_t*>(nullptr));
+  } else {
+    hipLaunchKernelGGL(mask_build_wide_kernel, dim3(std::min(B, 4096)), dim3(kWideThreads), 0, stream,
+                       parent, B, T, W, mask, static_cast<int32_t*>(nullptr));
+  }
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess && status != nullptr) {
+    hipLaunchKernelGGL(mask_status_kernel, dim3(1), dim3(64), 0, stream, parent, B, T, W, mask,
+                       status);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 }  // namespace ltree
