@@ -23,15 +23,15 @@ on the host cores.
 `--row NAME` measures one of the steps around the verification path instead
 (the draft's cross-attention into the target cache, its sliding-window
 self-attention, verification of a 256-node tree, verification over a paged
-cache, the KV-cache commit, the tree rotary embedding) and prints that row's
-own JSON line.
+cache, the KV-cache commit, the tree rotary embedding, one GPU's share of the
+layer under 8-way sharding) and prints that row's own JSON line.
 
 The default warm-up (1000 untimed steps, about 75 ms) lets the GPU settle
 at its sustained clocks; with 10 warm-up steps the timed steps run about 15%
 slower than the same steps a few tens of milliseconds later.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 1000] [--config 4]
-    python bench.py --row {xattn,window,bigtree,paged,commit,rope}
+    python bench.py --row {xattn,window,bigtree,paged,commit,rope,shard}
 """
 
 from __future__ import annotations
@@ -230,6 +230,87 @@ def row_xattn(args):
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": None,
                      "hbm_frac": round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+    }
+
+
+def row_shard(args):
+    """One GPU's share of the QwQ-shaped layer when the layer is sharded over
+    8 GPUs: KV-head (tensor) parallel, one KV head with its 5 query heads over
+    the whole 32768-key prefix; context parallel, all heads over the last
+    4096 prefix keys with the tree (the shard that holds the tree; the others
+    run the same call without it).  Each share is one ltree_attn call on this
+    GPU, graph-timed over rotating KV copies; the exchange between GPUs (none
+    for KV heads, one all-gather of the partials for the context split) is
+    not part of it."""
+    import math
+
+    import torch
+
+    import tree_attention_amd as ta
+    from workloads import make_config
+
+    w = make_config(4)
+    dev = "cuda:0"
+    B, T, Hq, D = w.q.shape
+    Hkv = w.k_prefix.shape[1]
+    G = Hq // Hkv
+    e = w.q.element_size()
+    mask_all = None
+    out = {}
+    shares = {
+        "kv_head_share": dict(q=w.q[:, :, :G], kp=w.k_prefix[:, :1], vp=w.v_prefix[:, :1],
+                              kt=w.k_tree[:, :, :1], vt=w.v_tree[:, :, :1],
+                              L=sum(w.prefix_lens)),
+        "context_share": dict(q=w.q, kp=w.k_prefix[-4096:], vp=w.v_prefix[-4096:], kt=w.k_tree,
+                              vt=w.v_tree, L=4096),
+    }
+    for name, sh in shares.items():
+        q = sh["q"].contiguous().to(dev)
+        kt, vt = sh["kt"].contiguous().to(dev), sh["vt"].contiguous().to(dev)
+        L = sh["L"]
+        hq, hkv = q.shape[2], kt.shape[2]
+        off = torch.tensor([0, L], dtype=torch.int32, device=dev)
+        kv_bytes = 2 * L * hkv * D * e
+        n = max(2, math.ceil(512e6 / kv_bytes))
+        kp0, vp0 = sh["kp"].contiguous().to(dev), sh["vp"].contiguous().to(dev)
+        kv = [(kp0, vp0)] + [(kp0.clone(), vp0.clone()) for _ in range(n - 1)]
+        if mask_all is None:
+            mask_all, _ = ta.build_mask(w.parent.to(dev))
+        o = torch.empty((B, T, hq, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, hq, T), dtype=torch.float32, device=dev)
+        ws = ta.workspace_for(q, kt, L)
+
+        def call(s):
+            kp, vp = kv[s % n]
+            return ta.ltree_attn(q, kp, vp, off, L, kt, vt, mask_all, o, lse, ws, w.scale)
+
+        for s in range(args.warmup):
+            assert call(s) == 0
+        torch.cuda.synchronize()
+        us = time_graph(call, args.steps)
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        anc = depth_sum(w.parent[0].tolist())
+        flop = 4 * D * hq * T * L + 4 * D * hq * anc
+        bytes_ = (2 * L * hkv * D * e + B * T * hq * D * e + 2 * B * T * hkv * D * e
+                  + B * T * hq * D * 4 + B * hq * T * 4)
+        tflops = flop / (us * 1e-6) / 1e12
+        out[name] = {"Hq": hq, "Hkv": hkv, "prefix_len": L, "us_per_call": round(us, 2),
+                     "tflops": round(tflops, 2), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "hbm_frac": round(bytes_ / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                     "cache": f"cold ({n} rotating KV copies)"}
+    kvs = out["kv_head_share"]
+    return {
+        "metric": "one GPU's share of the QwQ-shaped layer under 8-way sharding, µs/call + TFLOP/s",
+        "value": kvs["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(kvs["us_per_call"] / 1000, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), 1% of prefix rows x8)",
+        "config": {"workload": "shard-of-qwq32b-gqa40/8-d128-L32k-T64", "B": B, "T": T, "D": D,
+                   "shares": "KV head 0 (value); last 4096 prefix keys"},
+        **out,
+        "roofline": {"bound": "mfma", "achieved": kvs["tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": kvs["mfma_frac"], "traffic": None,
+                     "hbm_frac": kvs["hbm_frac"]},
     }
 
 
@@ -533,7 +614,7 @@ def row_rope(args):
 
 
 ROWS = {"xattn": row_xattn, "window": row_window, "bigtree": row_bigtree, "paged": row_paged,
-        "commit": row_commit, "rope": row_rope}
+        "commit": row_commit, "rope": row_rope, "shard": row_shard}
 
 
 def _kernel_kind(name: str):

@@ -19,7 +19,7 @@ def test_more_than_one_gpu_is_refused():
 def test_rows_are_known():
     sys.path.insert(0, ROOT)
     import bench
-    assert set(bench.ROWS) == {"xattn", "window", "bigtree", "paged", "commit", "rope"}
+    assert set(bench.ROWS) == {"xattn", "window", "bigtree", "paged", "commit", "rope", "shard"}
 
 
 def _write_trace(path, K, W, reps, partial_us=50.0, merge_us=7.0):

@@ -90,6 +90,41 @@ def test_config_all_rows(k):
     assert eo <= BF16_O_TOL and el <= LSE_TOL
 
 
+def _shard(w, name, heads=None, last_keys=None):
+    """One GPU's share of w under 8-way sharding: KV head heads[0] with its
+    query heads, or the last `last_keys` prefix keys with every head."""
+    from dataclasses import replace
+    Hq, Hkv = w.q.shape[2], w.k_tree.shape[2]
+    G = Hq // Hkv
+    if heads is not None:
+        g = heads
+        hs, kv = slice(g * G, (g + 1) * G), slice(g, g + 1)
+        return replace(w, name=name, q=w.q[:, :, hs].contiguous(),
+                       k_prefix=w.k_prefix[:, kv].contiguous(),
+                       v_prefix=w.v_prefix[:, kv].contiguous(),
+                       k_tree=w.k_tree[:, :, kv].contiguous(),
+                       v_tree=w.v_tree[:, :, kv].contiguous())
+    L = last_keys
+    return replace(w, name=name, k_prefix=w.k_prefix[-L:].contiguous(),
+                   v_prefix=w.v_prefix[-L:].contiguous(),
+                   offsets=torch.tensor([0, L], dtype=torch.int32), prefix_lens=[L])
+
+
+@pytest.mark.parametrize("share", ["kv_head_7", "context_last_4096"])
+def test_qwq_shape_one_gpu_share_all_rows(share):
+    """The shares `bench.py --row shard` times: KV head 7 alone (8-way tensor
+    parallel: 5 query heads over all 32768 keys, 128 splits of 256 keys) and
+    the last 4096 prefix keys with every head and the tree (8-way context
+    parallel)."""
+    w = make_config(4)
+    w = _shard(w, share, heads=7) if share.startswith("kv") else _shard(w, share, last_keys=4096)
+    say("one GPU share", share)
+    o, lse = _run_attn(w)
+    eo, el = _compare_all(w, o, lse, _tree_attn_refs(w))
+    _report(f"qwq share {share} ltree_attn", w, eo, el)
+    assert eo <= BF16_O_TOL and el <= LSE_TOL
+
+
 def test_qwq_shape_256_node_tree_all_rows():
     """QwQ-shaped layer with a 256-node tree (depth <= 12, branching <= 3):
     1280 query rows per KV head in four row blocks, four tree tiles."""
