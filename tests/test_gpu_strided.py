@@ -120,6 +120,35 @@ def test_padded_rows(name, kpad, vpad):
     _check(w, o, lse, o_ref, lse_ref)
 
 
+def test_single_kv_head_row_view():
+    """One KV head: a [rows, 1, D] view of a padded buffer whose size-one head
+    dimension carries the row stride (any stride is valid there)."""
+    import tree_attention_amd as ta
+    rng = np.random.default_rng(zlib.crc32(b"hkv1_view"))
+    w = make_workload(rng, B=2, T=24, Hq=8, Hkv=1, D=128, prefix_lens=[600, 130],
+                      trees=("bounded", 6, 3), dtype="bf16", name="hkv1_view")
+    dev = "cuda"
+    D, pad = 128, 40
+    rows = sum(w.prefix_lens)
+    views, flats = [], []
+    for x in (w.k_prefix, w.v_prefix):
+        buf = torch.randn(rows, D + pad).to(x.dtype)
+        buf[:, :D] = x.reshape(rows, D)
+        buf = buf.to(dev)
+        v = buf.view(rows, 1, D + pad)[:, :, :D]
+        assert v.stride(1) == D + pad
+        views.append(v)
+        flats.append(buf.cpu().float().numpy().reshape(-1))
+    mask, _ = ta.build_mask(w.parent.to(dev))
+    say("strided single KV head view")
+    o, lse = ta.attn_strided(w.q.to(dev), views[0], views[1], w.offsets.to(dev),
+                             max(w.prefix_lens), w.k_tree.to(dev), w.v_tree.to(dev), mask,
+                             w.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle_from_flat(w, flats[0], flats[1], D + pad, D + pad)
+    _check(w, o, lse, o_ref, lse_ref)
+
+
 def test_prefix_only():
     """Tree arguments NULL: attention over the strided prefix alone; an empty
     prefix gives o = 0 and lse = -inf."""

@@ -273,7 +273,9 @@ def _row_view(t, name, Hkv, D, dtype):
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.dim() != 3 or t.shape[1:] != (Hkv, D) or t.stride(2) != 1 or t.stride(1) != D:
+    # (a dimension of size one has no meaningful stride)
+    packed = (D == 1 or t.stride(2) == 1) and (Hkv == 1 or t.stride(1) == D)
+    if t.dim() != 3 or t.shape[1:] != (Hkv, D) or not packed:
         raise ValueError(f"{name} must be a [rows, Hkv, D] view with packed (Hkv, D)")
     return t.stride(0) if t.shape[0] > 1 else Hkv * D
 
