@@ -1,9 +1,10 @@
 """Seeded random problems across the combinations of the calls: tree size
 (below and above 64 nodes), GQA group, KV heads, head dimension, dtype,
-ragged prefix lengths (empty ones included), packed or paged cache (page
-sizes that are and are not multiples of 64), verification, prefix-only and
-window attention.  Each case is small enough for the oracle and is checked
-against it with the stated tolerances."""
+ragged prefix lengths (empty ones included), packed, paged (page sizes that
+are and are not multiples of 64) or strided cache (interleaved K/V, padded
+rows), verification, prefix-only and window attention, and the
+allocation-free call.  Each case is small enough for the oracle and is
+checked against it with the stated tolerances."""
 
 import numpy as np
 import pytest
@@ -112,6 +113,72 @@ def test_random_problem(seed):
     assert int(status.item()) == 0
     o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
     fin = np.isfinite(lse_ref)           # prefix-only rows of an empty prefix: -inf
+    assert np.array_equal(np.isfinite(lse), fin)
+    tol = BF16_O_TOL if c["dtype"] == "bf16" else F32_O_TOL
+    assert np.max(np.abs(o - o_ref)) <= tol, c
+    assert np.max(np.abs(lse[fin] - lse_ref[fin]), initial=0.0) <= LSE_TOL, c
+
+
+LAYOUTS = ["interleaved", "padded_k", "padded_both", "noalloc"]
+
+
+def _strided_views(w, layout, seed, dev="cuda"):
+    """Device views [rows, Hkv, D] of the prefix K and V in `layout`, holding
+    exactly w's packed rows (padding carries noise)."""
+    r = np.random.default_rng(seed)
+    rows, Hkv, D = w.k_prefix.shape
+    if layout == "interleaved":
+        kv = torch.stack([w.k_prefix, w.v_prefix], dim=1).contiguous().to(dev)
+        return kv[:, 0], kv[:, 1]
+    pads = (8 * int(r.integers(1, 9)), 0 if layout == "padded_k" else 8 * int(r.integers(1, 9)))
+    out = []
+    for x, pad in zip((w.k_prefix, w.v_prefix), pads):
+        buf = torch.randn(max(rows, 1), Hkv * D + pad).to(x.dtype)
+        buf[:rows, :Hkv * D] = x.reshape(rows, Hkv * D)
+        buf = buf.to(dev)
+        out.append(buf[:rows, :Hkv * D].view(rows, Hkv, D))
+    return out[0], out[1]
+
+
+@pytest.mark.parametrize("seed", range(100, 124))
+def test_random_layout_problem(seed):
+    """The same problem distribution over the prefix layouts of the strided
+    call (interleaved K/V, padded K rows, both padded by different amounts)
+    and over the allocation-free call; checked against the oracle on the
+    packed rows, which is what the layouts hold."""
+    import tree_attention_amd as ta
+    c = _draw(seed)
+    layout = LAYOUTS[seed % len(LAYOUTS)]
+    mode = "attn" if layout == "noalloc" or c["mode"] != "prefix" else "prefix"
+    rng = np.random.default_rng(seed)
+    w = make_workload(rng, B=c["B"], T=c["T"], Hq=c["G"] * c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+                      prefix_lens=c["lens"], trees=c["kind"], dtype=c["dtype"])
+    say("random layout problem", layout, mode, c)
+    dev = "cuda"
+    B, T, Hq, D = w.q.shape
+    L = max(w.prefix_lens)
+    d = {k: getattr(w, k).to(dev) for k in ("q", "k_prefix", "v_prefix", "offsets", "k_tree",
+                                             "v_tree", "parent")}
+    mask, status = ta.build_mask(d["parent"])
+    if mode == "attn":
+        o_ref, lse_ref = oracle.oracle_attn(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(),
+                                            w.k_tree, w.v_tree, w.parent.numpy(), w.scale)
+    else:
+        o_ref, lse_ref = oracle.oracle_prefix_attn(w.q, w.k_prefix, w.v_prefix,
+                                                   w.offsets.numpy(), w.scale)
+    if layout == "noalloc":
+        o = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, Hq, T), dtype=torch.float32, device=dev)
+        assert ta.ltree_attn_noalloc(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], L,
+                                     d["k_tree"], d["v_tree"], mask, o, lse, w.scale) == 0
+    else:
+        kv, vv = _strided_views(w, layout, seed)
+        tree = (d["k_tree"], d["v_tree"], mask) if mode == "attn" else (None, None, None)
+        o, lse = ta.attn_strided(d["q"], kv, vv, d["offsets"], L, *tree, w.scale)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse), fin)
     tol = BF16_O_TOL if c["dtype"] == "bf16" else F32_O_TOL
     assert np.max(np.abs(o - o_ref)) <= tol, c
