@@ -15,7 +15,8 @@
 //   o = sum_s (w_s / Z) o_s,  lse = ln 2 * (M + log2 Z).
 //
 // One wavefront per output row (b, h, i).  Lane s first loads the lse (and,
-// on the bf16 path, the scale) of partial s, 64 partials at a time; the
+// on the bf16 path, the scale) of partial s, 64 partials at a time (the
+// first 64 together with the prefix length, and kept in registers); the
 // wavefront reduces max and sum across lanes and forms each partial's weight
 // in its lane.  Then every lane owns D/64 consecutive features: per partial it
 // reads them (one coalesced row read per partial, several partials in flight)
@@ -89,6 +90,15 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   float* orow = o + ((static_cast<size_t>(b) * T + i) * Hq + h) * D + j * FPL;
   float* lrow = lse + (static_cast<size_t>(b) * Hq + h) * T + i;
 
+  const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
+  auto part_row = [&](int s) { return (base + s) * R + r; };
+  // the first kBatch partials' lse and scale, loaded together with the
+  // prefix length (slots below `slots` lie inside the workspace; what lies
+  // past the last partial is dropped below)
+  const bool pre = j < slots && j < kBatch;
+  float l0 = pre ? lse_part[part_row(j)] : -INFINITY;
+  float sc0 = (SNORM && pre) ? scale_part[part_row(j)] : 0.f;
+
   int start, n;
   const int L = seq_lens != nullptr ? seq_lens[b] : offsets[b + 1] - offsets[b];
   const float nan = __builtin_nanf("");
@@ -102,14 +112,16 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
   // one partial per prefix split, the last of which also covers the tree
   // keys; one tree-only partial when the prefix is empty
   const int nparts = n == 0 ? 1 : (n + chunk - 1) / chunk;
-  const size_t base = static_cast<size_t>(b * Hkv + g) * slots;
-  auto part_row = [&](int s) { return (base + s) * R + r; };
+  if (j >= nparts) {
+    l0 = -INFINITY;
+    sc0 = 0.f;
+  }
 
   // max and sum of 2^lse over all partials; a NaN partial (a paged split
   // with a page outside the pool) makes the row NaN
-  float mx = -INFINITY;
-  bool bad = false;
-  for (int s0 = 0; s0 < nparts; s0 += kBatch) {
+  float mx = l0;
+  bool bad = l0 != l0;
+  for (int s0 = kBatch; s0 < nparts; s0 += kBatch) {
     if (s0 + j < nparts) {
       const float l = lse_part[part_row(s0 + j)];
       bad = bad || l != l;
@@ -131,8 +143,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     if (j == 0) *lrow = -INFINITY;
     return;
   }
-  float z = 0.f;
-  for (int s0 = 0; s0 < nparts; s0 += kBatch) {
+  float z = exp2f(l0 - mx);
+  for (int s0 = kBatch; s0 < nparts; s0 += kBatch) {
     if (s0 + j < nparts) z += exp2f(lse_part[part_row(s0 + j)] - mx);
   }
   z = wave_sum(z);
@@ -145,7 +157,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void lse_merge_kernel(
     const int n = min(kBatch, nparts - s0);
     // this lane's weight: partial s0 + j
     float wl = 0.f;
-    if (j < n) {
+    if (s0 == 0) {
+      wl = exp2f(l0 - mx) * inv_z;
+      if constexpr (SNORM) wl *= sc0 * (1.f / 32767.f);
+    } else if (j < n) {
       const size_t pr = part_row(s0 + j);
       wl = exp2f(lse_part[pr] - mx) * inv_z;
       if constexpr (SNORM) wl *= scale_part[pr] * (1.f / 32767.f);
