@@ -1,7 +1,10 @@
 """The C ABI used from plain C: tests/c_abi/ltree_c_caller (built by
 tree_attention_amd/build.py) reads a seeded problem, calls ltree_build_mask
-and ltree_attn on hipMalloc'd buffers and writes the results, which must
-match the fp64 oracle: the mask bit-exact, o and lse within the tolerances."""
+and ltree_attn on hipMalloc'd buffers, then ltree_attn_noalloc and
+ltree_attn_strided over an interleaved copy of the prefix cache, and writes
+the results, which must match the fp64 oracle (the mask bit-exact, o and lse
+within the tolerances) and, for the two other calls, ltree_attn bit for bit
+(the same kernels in the same order)."""
 
 import os
 import subprocess
@@ -52,12 +55,21 @@ def test_c_caller_matches_oracle(dtype, T, D):
         Wd = (T + 63) // 64
         raw = open(dst, "rb").read()
     off = 0
-    rc = np.frombuffer(raw, np.int32, 2, off); off += 8
+    rc = np.frombuffer(raw, np.int32, 4, off); off += 16
     status = int(np.frombuffer(raw, np.int32, 1, off)[0]); off += 4
     mask = np.frombuffer(raw, np.uint64, B * T * Wd, off).reshape(B, T, Wd); off += 8 * B * T * Wd
-    o = np.frombuffer(raw, np.float32, B * T * Hq * D, off).reshape(B, T, Hq, D); off += 4 * o.size
-    lse = np.frombuffer(raw, np.float32, B * Hq * T, off).reshape(B, Hq, T)
-    assert rc.tolist() == [0, 0] and status == 0
+    res = []
+    for _ in range(3):  # ltree_attn, ltree_attn_noalloc, ltree_attn_strided
+        o = np.frombuffer(raw, np.float32, B * T * Hq * D, off).reshape(B, T, Hq, D)
+        off += 4 * o.size
+        lse = np.frombuffer(raw, np.float32, B * Hq * T, off).reshape(B, Hq, T)
+        off += 4 * lse.size
+        res.append((o, lse))
+    assert off == len(raw)
+    assert rc.tolist() == [0, 0, 0, 0] and status == 0
+    o, lse = res[0]
+    for o2, lse2 in res[1:]:
+        assert np.array_equal(o2, o) and np.array_equal(lse2, lse)
     assert np.array_equal(mask, oracle.oracle_mask(w.parent.numpy()))
     o_ref, lse_ref = oracle.oracle_attn(w.q, w.k_prefix, w.v_prefix, w.offsets.numpy(), w.k_tree,
                                         w.v_tree, w.parent.numpy(), w.scale)
