@@ -178,8 +178,8 @@ int ltree_attn(ltree_dtype dtype, int B, int T, int Hq, int Hkv, int D, float sc
  * Every call on one device shares that device's array: calls that overlap in
  * time on one device (on different streams, or from different threads with
  * their kernels still running) race and give wrong results.  Calls ordered on
- * one stream are safe.  Nothing in the array has to start at zero: the
- * partial kernel writes every value the merge reads.
+ * one stream are safe.  Nothing in the array has to start at zero: the merge
+ * uses only values the partial kernel wrote in the same call.
  *
  * Returns as ltree_attn, and LTREE_ERR_SCRATCH when
  * ltree_attn_workspace_bytes(B, T, Hq, Hkv, D, max_prefix_len) exceeds
