@@ -205,6 +205,47 @@ struct Ctx {
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
 };
 
+// The prefix keys of this workgroup's split (and whether the tree keys
+// follow them), from the sequence's entry in the prefix table.  False when
+// the split holds nothing: past the sequence's last split, or a length
+// outside the call's bounds (the merge reports that one).
+template <int D, int PAGED>
+__device__ inline bool locate(Ctx& x) {
+  const PartialArgs& a = *x.a;
+  const int off0 = PAGED ? 0 : a.offsets[x.b];
+  const int L = PAGED ? a.seq_lens[x.b] : a.offsets[x.b + 1] - off0;
+  int start, n;
+  if (!key_range(L, a.window, a.max_prefix_len, a.seq_cap, &start, &n)) return false;
+  // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
+  // (slot 0 when n = 0) also the tree keys
+  const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
+  if (x.slot >= nparts) return false;
+  const int k0 = x.slot * a.chunk;
+  x.npk = max(0, min(a.chunk, n - k0));
+  x.kfirst = start + k0;
+  x.tree = a.has_tree && x.slot == nparts - 1;
+  // window W: node i sees prefix keys from L - W + depth(i) on, i.e. from
+  // key n - W + depth(i) <= depth(i) - 1 of the range (within its first 64
+  // keys for trees of up to 64 nodes, its first 256 for larger ones)
+  x.head = a.window > 0 && x.npk > 0 && k0 < kHeadKeys;
+  x.hbase = n - a.window;
+  x.hk0 = k0;
+  // prefix rows at the caller's strides (a paged pool is packed: Hkv * D)
+  x.tstride = a.Hkv * D;
+  x.kstride = PAGED ? x.tstride : a.kstride;
+  x.vstride = PAGED ? x.tstride : a.vstride;
+  const size_t row0 = static_cast<size_t>(off0) + start + k0;
+  x.kbase = static_cast<const __bf16*>(a.kp) + row0 * x.kstride + x.g * D;
+  x.vbase = static_cast<const __bf16*>(a.vp) + row0 * x.vstride + x.g * D;
+  x.ktree = static_cast<const __bf16*>(a.kt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
+  x.vtree = static_cast<const __bf16*>(a.vt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
+  if (x.npk == 0) {  // tree only: the prefix pointers may not be dereferenceable
+    x.kbase = x.ktree;
+    x.vbase = x.vtree;
+  }
+  return true;
+}
+
 // The per-wave body: NT row tiles (rows rbase + 16*(wave + 8*rt) + l16).
 // WIN: the sliding-window variant (the head tile's per-row masking exists
 // only there, so the other variant's registers are not spent on it).
@@ -218,34 +259,48 @@ struct Ctx {
 // (any page size, a pool below 4 GB): one buffer spans the pool and every
 // lane finds its own row's page.
 template <int D, int NT, bool WIN, bool BIGT, int PAGED, bool STR>
-__device__ __attribute__((always_inline)) inline void run(const Ctx& x) {
+__device__ __attribute__((always_inline)) inline void run(Ctx& x) {
   using C = Cfg<D>;
   const PartialArgs& a = *x.a;
   const int lane = x.lane, l16 = x.l16, grp = x.grp, wave = x.wave, tid = x.tid;
-  const int npk = x.npk;
-  const bool tree = x.tree;
-  const bool head = WIN && x.head;
   const int T = x.a->T;
 
-  // ---- queries of this wave's rows, as the B operand (Q^T) of the QK MFMA
+  // ---- queries of this wave's rows, as the B operand (Q^T) of the QK MFMA,
+  // and (trees of up to 64 nodes) the rows' mask words.  Neither depends on
+  // the prefix table, so they are issued before it is read and the two
+  // memory latencies overlap.
   bf16x8 qf[NT][C::DC];
-  uint32_t vbits[NT];  // tree: this lane's mask bits (keys 8grp..8grp+7 of each block)
+  uint64_t mws[NT];
 #pragma unroll
   for (int rt = 0; rt < NT; ++rt) {
     // a row past the workgroup's rows reads the last real row (without a
     // branch per load): its results are never written
     const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
-    const bool ok = r < x.rend;
-    const int rr = ok ? r : x.rend - 1;
+    const int rr = r < x.rend ? r : x.rend - 1;
     const int i = rr / a.G;
     const int hh = rr % a.G;
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
                        ((static_cast<size_t>(x.b) * a.T + i) * a.Hq + x.g * a.G + hh) * D + grp * 8;
 #pragma unroll
     for (int c = 0; c < C::DC; ++c) qf[rt][c] = *reinterpret_cast<const bf16x8*>(qp + c * 32);
+    mws[rt] = (!BIGT && a.mask != nullptr) ? a.mask[static_cast<size_t>(x.b) * a.T + i] : 0;
+  }
+  // this workgroup's keys; none (a split past the sequence's last, or an
+  // invalid length, which the merge reports): nothing to do
+  if (!locate<D, PAGED>(x)) return;
+  const int npk = x.npk;
+  const bool tree = x.tree;
+  const bool head = WIN && x.head;
+
+  uint32_t vbits[NT];  // tree: this lane's mask bits (keys 8grp..8grp+7 of each block)
+#pragma unroll
+  for (int rt = 0; rt < NT; ++rt) {
+    const int r = x.rbase + 16 * (wave + kWaves * rt) + l16;
+    const bool ok = r < x.rend;
+    const int i = (ok ? r : x.rend - 1) / a.G;
     vbits[rt] = 0xffffu;
     if (!BIGT && (tree || head) && ok) {
-      const uint64_t mw = a.mask[static_cast<size_t>(x.b) * a.T + i];
+      const uint64_t mw = mws[rt];
       if (tree) {
         vbits[rt] = static_cast<uint32_t>((mw >> (8 * grp)) & 0xffu) |
                     (static_cast<uint32_t>((mw >> (32 + 8 * grp)) & 0xffu) << 8);
@@ -808,41 +863,11 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.b = blockIdx.z / a.row_blocks;
   const int rb = blockIdx.z % a.row_blocks;
   x.rbase = rb * a.rows_per_wg;
-  const int off0 = PAGED ? 0 : a.offsets[x.b];
-  const int L = PAGED ? a.seq_lens[x.b] : a.offsets[x.b + 1] - off0;
-  int start, n;
-  if (!key_range(L, a.window, a.max_prefix_len, a.seq_cap, &start, &n)) return;  // the merge reports it
-  // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
-  // (slot 0 when n = 0) also the tree keys
-  const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
-  if (x.slot >= nparts) return;
-  const int k0 = x.slot * a.chunk;
-  x.npk = max(0, min(a.chunk, n - k0));
-  x.kfirst = start + k0;
-  x.tree = a.has_tree && x.slot == nparts - 1;
-  // window W: node i sees prefix keys from L - W + depth(i) on, i.e. from
-  // key n - W + depth(i) <= depth(i) - 1 of the range (within its first 64
-  // keys for trees of up to 64 nodes, its first 256 for larger ones)
-  x.head = a.window > 0 && x.npk > 0 && k0 < kHeadKeys;
-  x.hbase = n - a.window;
-  x.hk0 = k0;
-  // prefix rows at the caller's strides (a paged pool is packed: Hkv * D)
-  x.tstride = a.Hkv * D;
-  x.kstride = PAGED ? x.tstride : a.kstride;
-  x.vstride = PAGED ? x.tstride : a.vstride;
-  const size_t row0 = static_cast<size_t>(off0) + start + k0;
-  x.kbase = static_cast<const __bf16*>(a.kp) + row0 * x.kstride + x.g * D;
-  x.vbase = static_cast<const __bf16*>(a.vp) + row0 * x.vstride + x.g * D;
-  x.ktree = static_cast<const __bf16*>(a.kt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
-  x.vtree = static_cast<const __bf16*>(a.vt) + (static_cast<size_t>(x.b) * a.T * a.Hkv + x.g) * D;
-  if (x.npk == 0) {  // tree only: the prefix pointers may not be dereferenceable
-    x.kbase = x.ktree;
-    x.vbase = x.vtree;
-  }
 
   // Row tiles of this workgroup and how many fall to this wave.  Every wave
   // runs the same sequence of tiles, blocks and barriers; only the number of
-  // row tiles it computes differs.
+  // row tiles it computes differs.  (Its keys are located inside run(),
+  // once the query loads are in flight.)
   x.rend = min(a.R, x.rbase + a.rows_per_wg);
   const int tiles = (x.rend - x.rbase + 15) / 16;
   const int ntw = (tiles - x.wave + kWaves - 1) / kWaves;  // tiles wave, wave+8, ... < tiles
