@@ -31,6 +31,9 @@ SMALL = {
     "fp32_d128": (2, 16, 8, 2, 128, [300, 77], "uniform", "f32"),
     "fp32_d64_forest": (1, 9, 6, 2, 64, [40], "forest", "f32"),
     "no_prefix_at_all": (2, 12, 4, 2, 128, [0, 0], "uniform", "bf16"),
+    # trees of 33-64 nodes after full and short last splits (256-key splits)
+    "tree_split_t40_b3": (3, 40, 8, 2, 128, [512, 500, 300], ("bounded", 6, 4), "bf16"),
+    "tree_split_t64_full": (1, 64, 10, 2, 128, [768], ("bounded", 8, 3), "bf16"),
 }
 
 

@@ -721,19 +721,25 @@ __device__ __attribute__((always_inline)) inline void run(Ctx& x) {
     // hides at most depth - 1 <= 255 of them; 63 for trees of up to 64 nodes)
     const int hb = (head && !tt && x.hk0 + t * kTile < kHeadKeys) ? x.hk0 + t * kTile : -1;
     const bool more = t + 1 < ntiles;
-    // both blocks always run: a block without real keys (the last tile may
-    // hold 32 or fewer) is fully masked, its probabilities are zero
+    // a tile whose real keys all lie in its first block (the last tile of a
+    // split, a tree of up to 32 nodes) skips the second: fully masked, it
+    // would add exact zeros
+    const bool two = !decltype(MASK_)::value || nk > 32;
     qk_softmax(I0{}, min(nk, 32), tt, hb, MASK_);
     pv(S, I0{}, [&] { kload(S, I1{}); });
-    qk_softmax(I1{}, nk - 32, tt, hb, MASK_);
+    if (two) qk_softmax(I1{}, nk - 32, tt, hb, MASK_);
     if (more) {
       wait_own(min(1, ntiles - 2 - t));
       convert(SN);
     }
     lds_barrier();
-    // (after the last tile this reads a stage nobody uses; harmless, and it
-    // keeps the P.V free of branches)
-    pv(S, I1{}, [&] { kload(SN, I0{}); });
+    // (after the last tile the K operand load reads a stage nobody uses;
+    // harmless)
+    if (two) {
+      pv(S, I1{}, [&] { kload(SN, I0{}); });
+    } else {
+      kload(SN, I0{});
+    }
     // stage S is free since the barrier; issued here rather than right after
     // it, the loads no longer hold up the P.V products of every wave at once
     if (t + 3 < ntiles) dma(S, t + 3);
