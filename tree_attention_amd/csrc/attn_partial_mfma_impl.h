@@ -562,12 +562,26 @@ __device__ __attribute__((always_inline)) inline void run(Ctx& x) {
   // get -inf
   // hk >= 0: a window head tile whose first key is key hk of the range
   auto qk = [&](f32x4 (&s)[2], int rt, int H, int valid, bool treeblk, int hk, auto MASK_) {
-#pragma unroll
-    for (int c = 0; c < C::DC; ++c)
+    if constexpr (D == 128) {
+      // the two accumulation chains (16-key halves) one after the other:
+      // products into the accumulator the previous one wrote issue sooner
+      // (1% fewer cycles per tile than alternating them)
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
-        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            ka[c][sub], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < C::DC; ++c) {
+          s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              ka[c][sub], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {  // (the D = 64 variants spill with that order)
+#pragma unroll
+      for (int c = 0; c < C::DC; ++c)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+          s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              ka[c][sub], qf[rt][c], c == 0 ? (f32x4){0.f, 0.f, 0.f, 0.f} : s[sub], 0, 0, 0);
+    }
     if constexpr (decltype(MASK_)::value) {
       // one bit per key of this lane: real key and (tree) an ancestor; made
       // opaque so the per-key conditions are formed here, not kept for the
