@@ -548,10 +548,11 @@ __device__ __attribute__((always_inline)) inline void run(Ctx& x) {
   bf16x8 ka[C::DC][2];
   auto kload = [&](int S, auto H_) {
     constexpr int H = decltype(H_)::value;
+    // (by 16-key half: the order in which the QK chains use them)
 #pragma unroll
-    for (int c = 0; c < C::DC; ++c)
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
+      for (int c = 0; c < C::DC; ++c)
         ka[c][sub] = *reinterpret_cast<const bf16x8*>(sm + koff[c] + S * C::BUF + H * 32 * C::ROW +
                                                       sub * 4 * C::ROW);
   };
@@ -690,14 +691,16 @@ __device__ __attribute__((always_inline)) inline void run(Ctx& x) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
         acc[dt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[dt], P[rt], acc[dt][rt], 0, 0, 0);
-    // issue order: two V^T reads ahead, then per d tile its products and one
-    // more read (the last two d tiles: the next block's K operands, DC each)
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    // issue order: three V^T reads ahead, then per d tile its products and
+    // one more read (the last two d tiles: the next block's K operands, DC
+    // each)
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-    for (int dt = 0; dt + 2 < C::DT; ++dt) {
+    for (int dt = 0; dt + 3 < C::DT; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) {
       __builtin_amdgcn_sched_group_barrier(0x008, NT, 0);
