@@ -31,15 +31,34 @@ constexpr int kMergeWaves = 4;  // rows per workgroup
 constexpr int kBatch = 64;      // partials per pass (one per lane)
 constexpr int kUnroll = 8;      // partial rows in flight per lane
 
+// Reductions over the wavefront without LDS round trips: the two halves and
+// the two 16-lane groups of each half are paired by lane swaps, then each
+// 16-lane row by rotations of 8, 4, 2 and 1 lanes (DPP).  Every pair combines
+// the same two values in every lane (addition is commutative), so all lanes
+// end with bitwise the same result.
+template <int K>
+__device__ inline float row_ror(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + K, 0xf, 0xf, false));
+}
 __device__ inline float wave_max(float v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v = fmaxf(v, __shfl_xor(v, s));
-  return v;
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
 }
 __device__ inline float wave_sum(float v) {
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s);
-  return v;
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
 }
 
 // lane s's value as a wavefront-uniform scalar
