@@ -61,7 +61,7 @@ def _pages(w, P, seed):
     return kp, vp, bt, torch.tensor(w.prefix_lens, dtype=torch.int32)
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_problem(seed):
     import tree_attention_amd as ta
     c = _draw(seed)
