@@ -146,6 +146,36 @@ def test_prefix_length_over_max_gives_nan():
     assert np.max(np.abs(lse[:2].double().numpy() - lse_ref[:2])) <= LSE_TOL
 
 
+@pytest.mark.parametrize("B", [256, 300])
+def test_large_ragged_batch(B):
+    """Many sequences of mixed lengths, every seventh empty and one longer than
+    max_prefix_len.  Batches of up to 256 sequences hand out their
+    (sequence, split) pairs in dispatch order, larger ones map workgroups to
+    them directly: either way every sequence gets exactly its own splits, the
+    long one NaN rows and the others the oracle's result."""
+    import tree_attention_amd as ta
+    rng = np.random.default_rng(B)
+    lens = rng.integers(1, 700, size=B)
+    lens[::7] = 0
+    bad = B // 2 + 1
+    lens[bad] = 900
+    w = make_workload(rng, B=B, T=6, Hq=4, Hkv=2, D=128, prefix_lens=lens.tolist(), trees="uniform",
+                      dtype="bf16")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    say("large ragged batch", B)
+    o, lse = ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 800, d["k_tree"],
+                     d["v_tree"], mask, w.scale)
+    torch.cuda.synchronize()
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    assert np.isnan(o[bad]).all() and np.isnan(lse[bad]).all()
+    keep = np.arange(B) != bad
+    o_ref, lse_ref = oracle_full(w)
+    assert np.all(np.isfinite(o[keep])) and np.all(np.isfinite(lse[keep]))
+    assert np.max(np.abs(o[keep] - o_ref[keep])) <= 2e-2
+    assert np.max(np.abs(lse[keep] - lse_ref[keep])) <= LSE_TOL
+
+
 def test_error_paths_with_real_tensors():
     import tree_attention_amd as ta
     w = _small("g2_t8_d64")

@@ -86,6 +86,9 @@ CASES = {
     "p48_bf16_d64": (2, 17, 8, 2, 64, [1000, 129], "uniform", "bf16", 48),
     "p16_bf16_t100": (2, 100, 8, 2, 128, [500, 64], ("bounded", 12, 4), "bf16", 16),
     "p32_fp32": (2, 16, 4, 2, 128, [300, 77], "forest", "f32", 32),
+    # a batch of 200 sequences (their splits handed out in dispatch order)
+    "p64_bf16_b200": (200, 8, 4, 2, 128, [int(n) for n in np.random.default_rng(200).integers(0, 500, 200)],
+                      "uniform", "bf16", 64),
 }
 
 

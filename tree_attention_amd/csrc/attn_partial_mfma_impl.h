@@ -17,6 +17,14 @@
 // chip's flop:byte balance point, which is why the rows are not split further.
 //
 // Grid (Hkv, slots, B * row_blocks), 512 threads = 8 wavefronts, two per SIMD.
+// One sequence: workgroup (g, s, rb) takes split s of row block rb.  A batch
+// of 2 to 256 sequences: the j-th workgroup of KV head g (j = y + slots * z)
+// takes the j-th (sequence, split) pair that exists, row blocks innermost,
+// so every workgroup with work comes before the empty ones in dispatch
+// order.  (Mapped directly, the unused slots of a short sequence would be
+// dispatched between the splits of the longer ones: each such workgroup
+// holds a CU for a memory round trip, and the CUs they leave are not the
+// ones the next real workgroups go to.)
 // The 16-row tiles of the workgroup's rows are dealt round-robin: tile t goes
 // to wave t % 8, so with 20 tiles (G*T = 320) waves 0-3 take three and waves
 // 4-7 two, and each SIMD (waves w and w+4) carries five.  Consecutive
@@ -89,6 +97,7 @@ constexpr int kPageStash = kMaxSplitPages * 4;  // LDS bytes, PAGED: the split's
 constexpr int kHeadKeys = 256;  // window: keys at the start of the range a row may hide
 // fourth word of a raw buffer descriptor (32-bit data format; no swizzle)
 constexpr int kBufferFlags = 0x00020000;
+constexpr int kCompactBatch = 256;  // batches of 2..256 sequences: splits packed in dispatch order
 
 template <int D>
 struct Cfg {
@@ -205,6 +214,62 @@ struct Ctx {
   int b, g, slot, rbase, rend;  // rows [rbase, rend) belong to this workgroup
 };
 
+// Splits of a sequence whose key range holds n keys: one per chunk, or one
+// (the tree's, or an empty partial) when n = 0.
+__device__ inline int split_count(int n, int chunk) { return n > 0 ? (n + chunk - 1) / chunk : 1; }
+
+// Batches of 2..kCompactBatch sequences: the (sequence, split) pair of
+// index p in the order (sequence, split), sequences whose length is out of
+// the call's bounds holding none.  Every wave computes it on its own (no
+// LDS, no barrier): lane l counts the splits of sequences 4l..4l+3, a
+// prefix sum over the lanes finds the lane and then the sequence that holds
+// pair p.  False when p is past the batch's last split.
+template <int PAGED>
+__device__ inline bool find_split(const PartialArgs& a, int lane, int p, int* b_out, int* s_out) {
+  int len[4];
+  if constexpr (PAGED != 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) len[k] = a.seq_lens[min(4 * lane + k, a.B - 1)];
+  } else {
+    int off[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) off[k] = a.offsets[min(4 * lane + k, a.B)];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) len[k] = off[k + 1] - off[k];
+  }
+  int np[4];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    int start, n;
+    const bool ok = 4 * lane + k < a.B &&
+                    key_range(len[k], a.window, a.max_prefix_len, a.seq_cap, &start, &n);
+    np[k] = ok ? split_count(n, a.chunk) : 0;
+    sum += np[k];
+  }
+  int inc = sum;  // splits of sequences 0 .. 4*lane+3
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int t = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += t;
+  }
+  const uint64_t hit = __ballot(inc > p);
+  if (hit == 0) return false;
+  const int l = __builtin_ctzll(hit);
+  int q = p - __builtin_amdgcn_readlane(inc - sum, l);  // index among lane l's splits
+  int b = 4 * l;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int n = __builtin_amdgcn_readlane(np[k], l);
+    if (q < n) break;
+    q -= n;
+    ++b;
+  }
+  *b_out = b;
+  *s_out = q;
+  return true;
+}
+
 // The prefix keys of this workgroup's split (and whether the tree keys
 // follow them), from the sequence's entry in the prefix table.  False when
 // the split holds nothing: past the sequence's last split, or a length
@@ -218,7 +283,7 @@ __device__ inline bool locate(Ctx& x) {
   if (!key_range(L, a.window, a.max_prefix_len, a.seq_cap, &start, &n)) return false;
   // slot s: prefix keys start + [s*chunk, min((s+1)*chunk, n)); the last one
   // (slot 0 when n = 0) also the tree keys
-  const int nparts = n > 0 ? (n + a.chunk - 1) / a.chunk : 1;
+  const int nparts = split_count(n, a.chunk);
   if (x.slot >= nparts) return false;
   const int k0 = x.slot * a.chunk;
   x.npk = max(0, min(a.chunk, n - k0));
@@ -882,9 +947,16 @@ __global__ __launch_bounds__(kThreads, 2) void partial_mfma_kernel(PartialArgs a
   x.l16 = x.lane & 15;
   x.grp = x.lane >> 4;
   x.g = blockIdx.x;
-  x.slot = blockIdx.y;
-  x.b = blockIdx.z / a.row_blocks;
-  const int rb = blockIdx.z % a.row_blocks;
+  int rb;
+  if (a.B > 1 && a.B <= kCompactBatch) {  // splits packed in dispatch order
+    const int j = blockIdx.y + gridDim.y * blockIdx.z;
+    if (!find_split<PAGED>(a, x.lane, j / a.row_blocks, &x.b, &x.slot)) return;
+    rb = j % a.row_blocks;
+  } else {
+    x.slot = blockIdx.y;
+    x.b = blockIdx.z / a.row_blocks;
+    rb = blockIdx.z % a.row_blocks;
+  }
   x.rbase = rb * a.rows_per_wg;
 
   // Row tiles of this workgroup and how many fall to this wave.  Every wave
