@@ -61,7 +61,7 @@ def _pages(w, P, seed):
     return kp, vp, bt, torch.tensor(w.prefix_lens, dtype=torch.int32)
 
 
-@pytest.mark.parametrize("seed", range(64))
+@pytest.mark.parametrize("seed", range(256))
 def test_random_problem(seed):
     import tree_attention_amd as ta
     c = _draw(seed)
@@ -140,7 +140,7 @@ def _strided_views(w, layout, seed, dev="cuda"):
     return out[0], out[1]
 
 
-@pytest.mark.parametrize("seed", range(100, 124))
+@pytest.mark.parametrize("seed", range(100, 164))
 def test_random_layout_problem(seed):
     """The same problem distribution over the prefix layouts of the strided
     call (interleaved K/V, padded K rows, both padded by different amounts)
