@@ -55,6 +55,28 @@ def test_tree_rope(name, dtype, D, lens, trees, base):
     _check(w, kt, rk)
 
 
+@pytest.mark.parametrize("name,B,T,Hq,Hkv,D", [
+    # 50 tokens, 12 passes of 4 heads: 5 workgroups per token, the last with no pass
+    ("uneven_split", 1, 50, 40, 8, 128),
+    # 9 * 64 tokens, more than the compute units: one workgroup per token
+    ("many_tokens", 9, 64, 12, 4, 128),
+    # 18 passes of 8 heads (D 64) in one workgroup: two batches of loads
+    ("many_heads", 3, 100, 136, 8, 64),
+])
+def test_tree_rope_work_split(name, B, T, Hq, Hkv, D):
+    """The token's head passes shared by several workgroups, by one, or in
+    more than one batch of loads."""
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    lens = [int(x) for x in rng.integers(0, 5000, size=B)]
+    w = make_workload(rng, B=B, T=T, Hq=Hq, Hkv=Hkv, D=D, prefix_lens=lens, trees=("bounded", 9, 3),
+                      dtype="bf16", name=name)
+    say("tree rope work split", name)
+    q, kt = _run(w, 1e6)
+    rq, rk = oracle.oracle_tree_rope(w.q, w.k_tree, w.parent.numpy(), w.offsets.numpy(), 1e6)
+    _check(w, q, rq)
+    _check(w, kt, rk)
+
+
 def test_tree_rope_qwq_shape():
     """The QwQ-shaped tree after the 32768-key prefix, rotary base 10^6."""
     w = make_config(4)
