@@ -176,6 +176,21 @@ def test_large_ragged_batch(B):
     assert np.max(np.abs(lse[keep] - lse_ref[keep])) <= LSE_TOL
 
 
+def test_every_prefix_over_max_gives_nan():
+    """Every sequence longer than max_prefix_len: no split exists, every
+    workgroup of the partial kernel finds none and returns, and every row is
+    NaN."""
+    import tree_attention_amd as ta
+    w = _small("tree_split_t40_b3")
+    d = to_device(w)
+    mask, _ = ta.build_mask(d["parent"])
+    say("every L_b over max_prefix_len")
+    o, lse = ta.attn(d["q"], d["k_prefix"], d["v_prefix"], d["offsets"], 200, d["k_tree"],
+                     d["v_tree"], mask, w.scale)
+    torch.cuda.synchronize()
+    assert torch.isnan(o.cpu()).all() and torch.isnan(lse.cpu()).all()
+
+
 def test_error_paths_with_real_tensors():
     import tree_attention_amd as ta
     w = _small("g2_t8_d64")

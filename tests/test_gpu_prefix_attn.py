@@ -25,6 +25,8 @@ SMALL = {
     "t1_decode_d64": (2, 1, 8, 2, 64, [257, 64], "bf16"),
     "fp32_d128": (2, 8, 4, 2, 128, [300, 77], "f32"),
     "fp32_d64_empty": (2, 5, 6, 3, 64, [0, 40], "f32"),
+    # every prefix empty: one empty partial per sequence, o = 0 and lse = -inf everywhere
+    "all_empty_b5": (5, 8, 4, 2, 128, [0, 0, 0, 0, 0], "bf16"),
 }
 
 
